@@ -1,0 +1,212 @@
+"""Benchmark of the BigBird block-sparse attention forward on one MI355X.
+
+One step = one ``bbsa_forward`` call (all kernels: the gathered-block
+attention kernel and the split-K merge of the two global query blocks) over
+one batch of the BigBird-base-shaped workload: B=4, H=12, L=4096, d=64,
+block=64, r=3, bf16, padded sequences, plan precomputed on the host (a layer
+builds its plan once).  Inputs are resident in HBM before timing starts; the
+steps rotate over several copies of the inputs (more bytes than the 256 MB
+last-level cache) so that no step reads its inputs from cache left by the
+previous one.
+
+Prints one JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd TFLOP/s (useful) + % MFMA/HBM roofline, L=4096 H=12"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (no sparsity)
+KERNEL_SOURCES = ["block_sparse_long_bbsa_amd/csrc/bbsa_forward.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bbsa_attn_bf16_B4_H12_L4096.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def useful_pairs(nb: int, r: int) -> int:
+    """Block pairs of one (batch, head) inside the pattern: 2 full rows, rows 1
+    and nb-2 with 4 + r blocks, the other nb - 4 middle rows with 5 + r."""
+    return 2 * nb + 2 * (4 + r) + (nb - 4) * (5 + r)
+
+
+def useful_flops(B, H, nb, block, d, r) -> float:
+    return 4.0 * block * block * d * useful_pairs(nb, r) * B * H
+
+
+def algorithmic_bytes(B, H, L, d, nb, r, elt) -> float:
+    """Q, K, V read once, O written once, the mask and the plan read once."""
+    return 4.0 * B * H * L * d * elt + B * L * 4 + H * (nb - 2) * r * 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, plan, w, budget_s: float):
+    """Time the oracle on a bounded sample: whole (batch, head) slices of the
+    same workload, as many as fit in about ``budget_s`` seconds."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    flops_per_slice = useful_flops(1, 1, w.nb, w.block, w.d, w.r)
+    done, t0 = 0, time.perf_counter()
+    b = 0
+    for h in range(w.H):
+        oracle.forward(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
+                       inp["v"][b:b + 1, h:h + 1], inp["mask"][b:b + 1], plan[h:h + 1], w.block)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops_per_slice * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} (batch, head) slices of {w.name}, float64 dense "
+                      f"masked attention, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the operator shards over (batch, head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_bbsa_amd import bbsa, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    elt = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log(f"workload {w.name}: generating inputs")
+    inp = workloads.make_inputs(args.workload)
+    plan = bbsa.bbsa_plan_rand_attn(w.H, w.nb, w.r, w.plan_seed)
+    dev = torch.device("cuda:0")
+    set_bytes = 4 * w.B * w.H * w.L * w.d * elt
+    n_sets = args.sets or max(1, int(np.ceil(768e6 / set_bytes)))
+    base = [torch.from_numpy(inp[n]).to(tdt).to(dev) for n in ("q", "k", "v")]
+    sets = []
+    for i in range(n_sets):
+        q, k, v = (t.clone() for t in base)
+        sets.append((q, k, v, torch.empty_like(q)))
+    mask = torch.from_numpy(inp["mask"]).to(dev)
+    ra = torch.from_numpy(plan).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        q, k, v, o = sets[i % n_sets]
+        bbsa.bbsa_forward(q, k, v, mask, ra, w.block, w.r, out=o, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Same steps again with the library's own HIP events around each kernel.
+    bbsa.bbsa_timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    main_ms, comb_ms, calls = bbsa.bbsa_timing_read()
+    bbsa.bbsa_timing_enable(False)
+    main_ms /= max(calls, 1)
+    comb_ms /= max(calls, 1)
+
+    flops = useful_flops(w.B, w.H, w.nb, w.block, w.d, w.r)
+    nbytes = algorithmic_bytes(w.B, w.H, w.L, w.d, w.nb, w.r, elt)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        achieved = nbytes / (main_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = flops / (main_ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"step {ms * 1e3:.2f} us; main kernel {main_ms * 1e3:.2f} us, merge {comb_ms * 1e3:.2f} us; "
+        f"{value:.1f} useful TFLOP/s; MFMA util {flops / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS:.3f}; "
+        f"HBM util {nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        cpu = cpu_baseline(inp, plan, w, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "block": w.block,
+                   "r": w.r, "useful_gflop_per_step": round(flops / 1e9, 3),
+                   "algorithmic_mb_per_step": round(nbytes / 1e6, 3), "input_sets": n_sets,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": read_traffic(),
+                     "kernel": "bbsa_attn_bf16", "kernel_us": round(main_ms * 1e3, 3),
+                     "merge_kernel_us": round(comb_ms * 1e3, 3),
+                     "mfma_frac": round(flops / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "hbm_frac": round(nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Small cases are compared over every output element; the five workloads at
+their full sizes are compared on every row of sampled query blocks (both
+global rows, their neighbours and middle rows), in the same launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_bbsa_amd import bbsa, workloads
+from gpu_helpers import (announce, assert_close, gather_rows, plans, run_gpu, sample_blocks,
+                         to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bbsa.lib()
+
+
+SMALL = [
+    # B, H, L, block, r, dtype, valid lengths (None = unpadded), seed
+    (2, 3, 1024, 64, 3, "bf16", (700, 1024), 1),
+    (1, 2, 768, 64, 3, "bf16", None, 2),          # smallest sparse length at r=3 (nb = 12)
+    (1, 2, 2048, 128, 2, "bf16", (1900,), 3),      # block 128, partial block
+    (2, 2, 4096, 64, 3, "bf16", (3072, 4000), 4),  # full rows split into 2 chunks
+    (1, 3, 1536, 64, 1, "bf16", None, 5),
+    (1, 2, 2560, 64, 5, "bf16", (2000,), 6),
+    (1, 1, 5120, 128, 3, "bf16", (4321,), 7),      # block 128, 40 blocks, chunked full rows
+    (1, 2, 1024, 64, 3, "f32", None, 8),
+    (2, 1, 2048, 128, 2, "f32", (1500, 2048), 9),
+    (1, 2, 4096, 64, 2, "f32", (3333,), 10),
+]
+
+
+@pytest.mark.parametrize("B,H,L,block,r,dtype,valid,seed", SMALL)
+def test_small_full_compare(B, H, L, block, r, dtype, valid, seed):
+    announce(f"small B{B} H{H} L{L} block{block} r{r} {dtype} valid={valid} seed={seed}")
+    inp = workloads.make_case(B, H, L, 64, seed, dtype=dtype, valid=valid)
+    cplan, oplan = plans(H, L // block, r, seed)
+    got, st = run_gpu(inp, block, r, dtype, cplan)
+    assert st == bbsa.BBSA_OK
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block)
+    assert_close(got, want, dtype, f"small L{L}")
+
+
+FALLBACK = [
+    (1, 2, 704, 64, 3, "bf16", (650,)),    # (5 + 2*3) * 64 = 704: full attention
+    (2, 1, 1152, 128, 2, "bf16", None),    # (5 + 2*2) * 128
+    (1, 1, 2880, 64, 20, "bf16", (2800,)), # 45 blocks: full rows are chunked and merged
+    (1, 2, 448, 64, 1, "f32", None),
+]
+
+
+@pytest.mark.parametrize("B,H,L,block,r,dtype,valid", FALLBACK)
+def test_short_sequence_falls_back_to_full_attention(B, H, L, block, r, dtype, valid):
+    announce(f"fallback B{B} H{H} L{L} block{block} r{r} {dtype}")
+    inp = workloads.make_case(B, H, L, 64, 11, dtype=dtype, valid=valid)
+    got, st = run_gpu(inp, block, r, dtype, None)
+    assert st == bbsa.BBSA_OK_FULL_FALLBACK
+    want = oracle.full_attention(inp["q"], inp["k"], inp["v"], inp["mask"])
+    assert_close(got, want, dtype, f"fallback L{L}")
+
+
+def test_fallback_boundary_status():
+    # 704 falls back, 768 does not (block 64, r 3).
+    for L, want in ((704, bbsa.BBSA_OK_FULL_FALLBACK), (768, bbsa.BBSA_OK)):
+        announce(f"boundary L{L}")
+        inp = workloads.make_case(1, 1, L, 64, 12)
+        plan = bbsa.bbsa_plan_rand_attn(1, L // 64, 3, 0) if L > 704 else None
+        _, st = run_gpu(inp, 64, 3, "bf16", plan)
+        assert st == want
+
+
+def test_null_mask_equals_all_ones_mask():
+    announce("null mask")
+    inp = workloads.make_case(2, 2, 2048, 64, 13)
+    cplan, _ = plans(2, 32, 3, 3)
+    a, _ = run_gpu(inp, 64, 3, "bf16", cplan, use_mask=True)
+    b, _ = run_gpu(inp, 64, 3, "bf16", cplan, use_mask=False)
+    assert np.array_equal(a, b)
+
+
+def test_batch_independence_bitwise():
+    announce("batch independence")
+    inp = workloads.make_case(3, 2, 2048, 64, 14, valid=(2048, 1111, 1800))
+    cplan, _ = plans(2, 32, 3, 5)
+    whole, _ = run_gpu(inp, 64, 3, "bf16", cplan)
+    for b in range(3):
+        one = {kk: inp[kk][b:b + 1] for kk in ("q", "k", "v", "mask")}
+        alone, _ = run_gpu(one, 64, 3, "bf16", cplan)
+        assert np.array_equal(alone[0], whole[b]), b
+
+
+def test_deterministic_bitwise():
+    announce("determinism")
+    inp = workloads.make_case(2, 4, 4096, 64, 15, valid=(4096, 3500))
+    cplan, _ = plans(4, 64, 3, 6)
+    a, _ = run_gpu(inp, 64, 3, "bf16", cplan)
+    b, _ = run_gpu(inp, 64, 3, "bf16", cplan)
+    assert np.array_equal(a, b)
+
+
+def test_fully_padded_sequence_matches_oracle():
+    # Every key padded: the constant -10000 cancels; rows are plain softmax.
+    announce("fully padded")
+    inp = workloads.make_case(1, 2, 1024, 64, 16, valid=(0,))
+    cplan, oplan = plans(2, 16, 3, 7)
+    got, _ = run_gpu(inp, 64, 3, "bf16", cplan)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64)
+    assert_close(got, want, "bf16", "fully padded")
+
+
+def test_out_of_range_plan_stays_in_bounds():
+    # Indices are clamped: no fault, finite output (result unspecified).
+    announce("clamped plan")
+    inp = workloads.make_case(1, 2, 1024, 64, 17)
+    bad = np.full((2, 14, 3), 10**6, dtype=np.int32)
+    bad[1] = -5
+    got, st = run_gpu(inp, 64, 3, "bf16", bad)
+    assert st == bbsa.BBSA_OK and np.isfinite(got).all()
+
+
+def test_output_guard_regions_untouched():
+    announce("guard regions")
+    inp = workloads.make_case(1, 2, 1024, 64, 18, valid=(900,))
+    cplan, oplan = plans(2, 16, 3, 8)
+    q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    mask = to_dev(inp["mask"], torch.float32)
+    n = q.numel()
+    big = torch.full((n + 2 * 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[4096:4096 + n].view(q.shape)
+    bbsa.bbsa_forward(q, k, v, mask, torch.from_numpy(cplan).cuda(), 64, 3, out=out)
+    torch.cuda.synchronize()
+    assert (big[:4096] == 7.0).all() and (big[4096 + n:] == 7.0).all()
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64)
+    assert_close(out.float().cpu().numpy().astype(np.float64), want, "bf16", "guarded")
+
+
+@pytest.mark.parametrize("wid,seed", [(1, None), (2, None), (3, None), (3, 1), (4, None), (5, None)])
+def test_workload_parity(wid, seed):
+    w = workloads.WORKLOADS[wid]
+    plan_seed = w.plan_seed if seed is None else seed
+    announce(f"workload {wid} {w.name} plan seed {plan_seed}")
+    inp = workloads.make_inputs(wid)
+    cplan, oplan = plans(w.H, w.nb, w.r, plan_seed)
+    got, st = run_gpu(inp, w.block, w.r, w.dtype, cplan)
+    assert st == bbsa.BBSA_OK
+    if wid == 1:
+        want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, w.block)
+        assert_close(got, want, w.dtype, w.name)
+        return
+    blocks = sample_blocks(w.nb)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, w.block,
+                          query_blocks=blocks)
+    assert_close(gather_rows(got, blocks, w.block), want, w.dtype, f"{w.name} sampled")
+    # valid rows only (rows past the valid length are discarded by callers)
+    assert np.isfinite(got).all()

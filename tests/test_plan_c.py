@@ -1,0 +1,57 @@
+"""The library's C++ planner against the oracle planner: bit-exact (CPU only)."""
+import numpy as np
+import pytest
+
+from oracle.planner import plan_rand_attn as oracle_plan
+
+bbsa = pytest.importorskip("block_sparse_long_bbsa_amd.bbsa")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return bbsa.lib()
+    except RuntimeError as e:          # library not built
+        pytest.skip(str(e))
+
+
+@pytest.mark.parametrize("H", [1, 12, 16])
+@pytest.mark.parametrize("nb,r", [(12, 1), (12, 3), (16, 3), (20, 5), (33, 2), (64, 3)])
+def test_c_planner_matches_oracle_grid(lib, H, nb, r):
+    for seed in range(0, 100, 7):
+        c = bbsa.bbsa_plan_rand_attn(H, nb, r, seed)
+        assert np.array_equal(c, oracle_plan(H, nb, r, seed)), (H, nb, r, seed)
+
+
+@pytest.mark.parametrize("H,nb,r,seed", [(12, 256, 3, 0), (16, 256, 2, 0), (16, 64, 3, 1),
+                                         (16, 64, 3, 15), (12, 64, 3, 0), (2, 16, 3, 1),
+                                         (1, 128, 5, 2**64 - 1)])
+def test_c_planner_matches_oracle_workload_plans(lib, H, nb, r, seed):
+    assert np.array_equal(bbsa.bbsa_plan_rand_attn(H, nb, r, seed), oracle_plan(H, nb, r, seed))
+
+
+def test_layer_seeds_0_to_15(lib):
+    for seed in range(16):
+        assert np.array_equal(bbsa.bbsa_plan_rand_attn(16, 64, 3, seed), oracle_plan(16, 64, 3, seed))
+
+
+def test_c_check_accepts_plans_and_rejects_violations(lib):
+    ra = bbsa.bbsa_plan_rand_attn(4, 20, 3, 9)
+    assert bbsa.bbsa_check_rand_attn(ra, 20, 3) == bbsa.BBSA_OK
+    bad = ra.copy(); bad[2, 5, 1] = bad[2, 5, 0]
+    assert bbsa.bbsa_check_rand_attn(bad, 20, 3) == bbsa.BBSA_ERR_PLAN
+    bad = ra.copy(); bad[0, 0, 0] = 2          # row 1: window {0,1,2}
+    assert bbsa.bbsa_check_rand_attn(bad, 20, 3) == bbsa.BBSA_ERR_PLAN
+    bad = ra.copy(); bad[3, 17, 2] = 19        # last block is not a middle block
+    assert bbsa.bbsa_check_rand_attn(bad, 20, 3) == bbsa.BBSA_ERR_PLAN
+    bad = ra.copy(); bad[1, 9, 0] = 0
+    assert bbsa.bbsa_check_rand_attn(bad, 20, 3) == bbsa.BBSA_ERR_PLAN
+
+
+def test_c_planner_argument_errors(lib):
+    with pytest.raises(bbsa.BbsaError) as e:
+        bbsa.bbsa_plan_rand_attn(1, 7, 3, 0)
+    assert e.value.status == bbsa.BBSA_ERR_SHAPE
+    with pytest.raises(bbsa.BbsaError) as e:
+        bbsa.bbsa_plan_rand_attn(1, 16, 0, 0)
+    assert e.value.status == bbsa.BBSA_ERR_ARG
