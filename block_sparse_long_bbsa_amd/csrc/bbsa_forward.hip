@@ -9,27 +9,28 @@
 // additive -10000; each query row takes a softmax over the keys it attends.
 //
 // How it is computed here (the pages' five-segment einsum layout is not used):
-//   * one wavefront owns 64 query rows (a "query tile") of one query block and
-//     walks a list of key blocks in steps of 32 keys;
-//   * scores are computed transposed, S^T = K Q^T, on MFMA 16x16x32 bf16, so
-//     that each lane holds all of its queries' scores for 8 keys and the row
-//     max needs only two cross-lane swaps (v_permlane32/16_swap);
-//   * K goes from HBM straight into MFMA operand registers (16-byte loads);
-//     V goes through LDS in an XOR-swizzled row-major tile and is read back
+//   * one wavefront (one 64-thread workgroup) owns 64 query rows of one query
+//     block and walks the item's key blocks in steps of 32 keys;
+//   * bf16 path: scores are computed transposed, S^T = K Q^T, on MFMA
+//     32x32x16 bf16, so each lane holds 16 keys of one query column and the
+//     row max needs a single cross-lane swap; Q is pre-scaled by log2(e) and
+//     the running reference max is subtracted for free by feeding a broadcast
+//     (-max) tuple as the MFMA accumulator input, so a probability costs one
+//     v_exp_f32;
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+//     XOR-swizzled rows); K is read back as the MFMA A operand, V is read back
 //     transposed with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T;
-//   * P is rounded to bf16 in registers and used directly as the B operand
-//     (the lane layout of the S^T accumulator matches it after a fixed
-//     permutation of the key order inside each 32-key step);
-//   * online softmax in base 2 with a lazy rescale (the running reference max
-//     moves only when a new max exceeds it by more than 2^8 in probability);
+//     P is rounded to bf16 in registers and used directly as the B operand;
+//   * software pipeline: the softmax of step j runs between the MFMAs of
+//     S(j+1) and of the PV product of step j-1; K tiles are fetched two steps
+//     ahead, V tiles one step ahead;
+//   * online softmax in base 2 with a lazy rescale (the reference max moves
+//     only when a score exceeds it by more than 8, i.e. p > 2^8);
 //   * the two global query blocks are split along the keys into chunks whose
-//     partial (O, max, sum) go to a workspace and are merged by a second
+//     partials (O, max, sum) go to a workspace and are merged by a second
 //     kernel with the log-sum-exp rule;
-//   * the bf16 kernel is persistent: each wavefront pulls work items from the
-//     queue of its own XCD (items of the (batch, head) pairs assigned to that
-//     XCD, so they share its L2) and streams through them without draining
-//     its pipeline: the next item's Q and first K/V tiles are fetched while
-//     the current item's last step computes.
+//   * workgroups are mapped onto the 8 XCDs so that all items of one
+//     (batch, head) run on one XCD and share its L2.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -45,9 +46,10 @@ namespace {
 typedef __bf16 bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kD = 64;        // head dimension
@@ -57,8 +59,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPadBias = -10000.0f;
 // Lazy rescale threshold (raw score units): unnormalised probabilities stay <= 2^8.
 constexpr float kTau = 8.0f / 1.4426950408889634f;
+constexpr float kTauLog2 = 8.0f;
 constexpr float kInitMax = -1.0e30f;
-// One split-K partial: O[64][64] fp32, then the 64 reference maxima, then the 64 sums.
+// One split-K partial: O[64][64] fp32, then the 64 reference maxima (log2
+// units), then the 64 row sums.
 constexpr int kPartialFloats = kQT * kD + 2 * kQT;
 
 struct Params {
@@ -77,30 +81,27 @@ struct Params {
   int items_per_bh;          // n_global_items + middle items
   int bh_total;              // B * H
   int xcd_remap;             // 1: map workgroups so one (batch, head) stays on one XCD
-  int *ctrl;                 // work-queue counters (see the control block layout below)
-  int n_waves;               // persistent wavefronts launched
 };
 
-// Control block (int32): queue counter of XCD class x at ctrl[32 * x]
-// (x = 0..7, one 128-byte line each), finished-wavefront counter at
-// ctrl[kDoneSlot].  All zero between calls: the last wavefront to finish
-// resets them.
-constexpr int kQueueStride = 32;
-constexpr int kDoneSlot = 8 * kQueueStride;
-constexpr int kCtrlInts = kDoneSlot + kQueueStride;
-
+// A work item: 64 query rows (query tile qt of query block qblock) of one
+// (batch, head), against either the middle row's key blocks or one chunk of
+// a full row.
 struct Item {
   int bh;
-  int qblock;     // query block index
-  int qt;         // query tile inside the block
+  int qblock;
+  int qt;
   int grow;       // full-row index (partials), -1 for a middle row
   int chunk;      // key chunk of a full row
 };
 
+// Workgroup -> item.  Items of one (batch, head) are numbered full-row chunks
+// first (the longest items start first), then middle rows in order.  With the
+// XCD remap, workgroup w runs on XCD w % 8 and takes the (w / 8)-th item of
+// the (batch, head) pairs x, x + 8, x + 16, ... (x = w % 8), so all items of
+// one pair share one L2.
 __device__ inline Item decode_item(const Params &p, int wg) {
   int bh, local;
   if (p.xcd_remap) {
-    // Workgroups are dispatched round-robin over the 8 XCDs: wg % 8 is the XCD.
     const int xcd = wg & 7, slot = wg >> 3;
     bh = xcd + 8 * (slot / p.items_per_bh);
     local = slot % p.items_per_bh;
@@ -121,76 +122,6 @@ __device__ inline Item decode_item(const Params &p, int wg) {
   it.qblock = global_row ? ((p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow)
                          : 1 + m / p.qtiles;
   return it;
-}
-
-// Items of XCD class x: the (batch, head) pairs bh = x, x + 8, ... in order,
-// each contributing items_per_bh items (full-row chunks first).
-__device__ inline int class_items(const Params &p, int x) {
-  const int nbh = (p.bh_total > x) ? (p.bh_total - x + 7) / 8 : 0;
-  return nbh * p.items_per_bh;
-}
-
-__device__ inline Item item_from_ticket(const Params &p, int ticket) {
-  const int x = ticket & 7, k = ticket >> 3;
-  const int bh = x + 8 * (k / p.items_per_bh);
-  const int local = k % p.items_per_bh;
-  const bool global_row = local < p.n_global_items;
-  const int per_row = p.qtiles * p.chunks;
-  const int m = local - p.n_global_items;
-  const int grow = global_row ? local / per_row : -1;
-  const int rem = global_row ? local % per_row : 0;
-  Item it;
-  it.bh = bh;
-  it.grow = grow;
-  it.qt = global_row ? rem / p.chunks : m % p.qtiles;
-  it.chunk = global_row ? rem % p.chunks : 0;
-  it.qblock = global_row ? ((p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow)
-                         : 1 + m / p.qtiles;
-  return it;
-}
-
-// Claim the next item: first from the home XCD's queue, then from the others.
-// Returns a ticket (k * 8 + class) or -1 when every queue is drained.  Only
-// lane 0 touches the counters; the result is broadcast.
-__device__ inline int claim_item(const Params &p, int home, int first_try) {
-  int ticket = -1;
-  if (__builtin_amdgcn_workitem_id_x() == 0) {
-    int k = first_try;
-    if (k >= 0 && k < class_items(p, home)) {
-      ticket = k * 8 + home;
-    } else {
-      for (int d = 1; d < 8; ++d) {
-        const int x = (home + d) & 7;
-        const int n = class_items(p, x);
-        int *q = p.ctrl + kQueueStride * x;
-        if (n == 0 || __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
-        k = __hip_atomic_fetch_add(q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (k < n) { ticket = k * 8 + x; break; }
-      }
-    }
-  }
-  return __builtin_amdgcn_readfirstlane(ticket);
-}
-
-// Start a claim on the home queue: returns the raw counter value (lane 0; other
-// lanes -1).  Resolved later by claim_item.
-__device__ inline int claim_issue(const Params &p, int home) {
-  int k = -1;
-  if (__builtin_amdgcn_workitem_id_x() == 0)
-    k = __hip_atomic_fetch_add(p.ctrl + kQueueStride * home, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return k;
-}
-
-// The last wavefront to finish puts the control block back to zero for the next call.
-__device__ inline void wave_exit(const Params &p) {
-  if (__builtin_amdgcn_workitem_id_x() == 0) {
-    const int old = __hip_atomic_fetch_add(p.ctrl + kDoneSlot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == p.n_waves - 1) {
-      for (int x = 0; x < 8; ++x)
-        __hip_atomic_store(p.ctrl + kQueueStride * x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.ctrl + kDoneSlot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 }
 
 __device__ inline float group4_max(float x) {
@@ -322,30 +253,32 @@ __device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
   const int lane = (int)__builtin_amdgcn_workitem_id_x();
   KeyWalk w;
   w.steps_per_block = p.block / kStep;
-  if (it.grow < 0) {
+  // Uniform quantities first (kept in scalar registers), then the per-lane list.
+  const bool middle = it.grow < 0;
+  const int i = it.qblock;
+  const int nw = (i == 1 || i == p.nb - 2) ? 2 : 3;
+  const int first = it.chunk * p.chunk_blocks;
+  const int nblk = middle ? 2 + nw + p.r : min(p.chunk_blocks, p.nb - first);
+  w.n_steps = __builtin_amdgcn_readfirstlane(nblk * w.steps_per_block);
+  int blk;
+  if (middle) {
     // Middle query block i: the two global blocks, the window without them,
     // then the random blocks (clamped so a bad plan never reads outside).
-    const int i = it.qblock;
-    const int nw = (i == 1 || i == p.nb - 2) ? 2 : 3;
     const int w0 = (i == 1) ? 1 : i - 1;
     const int h = it.bh % p.H;
     const int32_t *ra_row = p.rand_attn + ((int64_t)h * (p.nb - 2) + (i - 1)) * p.r;
-    int blk = 0;
+    blk = 0;
     if (lane == 1) blk = p.nb - 1;
     else if (lane >= 2 && lane < 2 + nw) blk = w0 + (lane - 2);
     else if (lane >= 2 + nw && lane < 2 + nw + p.r) blk = min(max(ra_row[lane - 2 - nw], 0), p.nb - 1);
-    w.blk = blk;
-    w.n_steps = (2 + nw + p.r) * w.steps_per_block;
   } else {
-    const int first = it.chunk * p.chunk_blocks;
-    const int nblk = min(p.chunk_blocks, p.nb - first);
-    w.blk = first + min(lane, nblk - 1);
-    w.n_steps = nblk * w.steps_per_block;
+    blk = first + min(lane, nblk - 1);
   }
+  w.blk = blk;
   return w;
 }
 
-// Finish an item: either normalise and store the output rows, or store a
+// Finish an item of the fp32 path: either normalise and store the output rows, or store a
 // split-K partial (unnormalised O, reference max, row sum).
 template <typename OutT>
 __device__ inline void finish_item(const Params &p, const Item &it, int q0, SoftmaxState &st,
@@ -365,7 +298,7 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, Soft
     if (g == 0) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        part[kQT * kD + 16 * nt + c] = st.m[nt];
+        part[kQT * kD + 16 * nt + c] = st.m[nt] * kLog2e;   // log2 units
         part[kQT * kD + kQT + 16 * nt + c] = lsum[nt];
       }
     }
@@ -390,80 +323,24 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, Soft
 
 // ---------------------------------------------------------------- bf16 path
 //
-// Per wavefront, LDS holds two K tiles and two V tiles of 32 keys x 64 d bf16,
-// row-major, 128 B per key row.  Tiles are filled straight from HBM with
-// global_load_lds_dwordx4 (lane l of an instruction writes the 16 bytes at
-// tile + 1024u + 16l, i.e. key row 8u + l/8, chunk position l%8) and stored
-// XOR-swizzled: the 16-byte chunk j of row k sits at position j ^ f(k).
-//   K: f(k) = (k & 7) ^ ((k >> 3) & 1) -- the 16-byte A-operand reads of 16
-//      consecutive rows hit distinct banks.
-//   V: f(k) = ((k >> 1) & 3) << 1     -- the 8-byte transposed reads
-//      (ds_read_b64_tr_b16) of 16 consecutive rows spread evenly over banks.
-//
-// Software pipeline of one item (steps j = 0 .. n-1 of 32 keys):
-//   iteration j: softmax of step j (vector ALUs) runs interleaved with
-//   S(j+1) = K(j+1) Q^T and O^T += V(j-1)^T P(j-1) (matrix cores).
-// K tiles are fetched two steps ahead, V tiles one step ahead.
+// LDS per wavefront: two K tiles and two V tiles of 32 keys x 64 d bf16,
+// row-major (128 B per key row).  Tiles are filled straight from HBM with
+// global_load_lds_dwordx4: lane l of instruction u writes the 16 bytes at
+// tile + 1024u + 16l (key row 8u + l/8, chunk position l%8).  The 16-byte
+// chunk j of key row k is stored at position j ^ f(k):
+//   K: f(k) = ((k >> 1) & 7) ^ ((k & 1) << 2) -- the 16-byte A-operand reads
+//      (row c, chunk 2k + h) of 8 or 16 consecutive rows hit distinct banks;
+//   V: f(k) = ((k >> 1) & 1) << 2             -- the 8-byte transposed reads
+//      (rows 16s + 8r + 0..7, 64 contiguous bytes each) spread evenly.
 constexpr int kTileBytes = kStep * kD * 2;          // 4 KB
-__device__ inline int k_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ inline int v_swz(int row) { return ((row >> 1) & 3) << 1; }
+__device__ inline int k_swz(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+__device__ inline int v_swz(int row) { return ((row >> 1) & 1) << 2; }
 
 typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
 
 __device__ inline void dma16(const void *src, unsigned char *lds_dst) {
   __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_dst, 16, 0, 0);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Row sums of the bf16-rounded probabilities (the values the PV product uses):
-// one v_dot2 against (1, 1) per pair.
-__device__ inline void row_sum_bf16(const bf16x8 (&pf)[4], SoftmaxState &st) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    float acc = st.l[nt];
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt], pf[nt], 0, 1), ones, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt], pf[nt], 2, 3), ones, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt], pf[nt], 4, 5), ones, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt], pf[nt], 6, 7), ones, acc, false);
-    st.l[nt] = acc;
-  }
-}
-
-// Rescale decision for one step (before its exponentials): moves the
-// reference max of the queries that need it and rescales their row sums;
-// returns whether the O accumulator must be rescaled by `alpha` once the
-// PV product still in flight has been added.
-__device__ inline bool rescale_decide(const f32x4 (&s)[2][4], SoftmaxState &st, float (&alpha)[4]) {
-  float mloc[4];
-  bool need = false;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    float a = __builtin_fmaxf(__builtin_fmaxf(s[0][nt][0], s[0][nt][1]), s[0][nt][2]);
-    a = __builtin_fmaxf(__builtin_fmaxf(a, s[0][nt][3]), s[1][nt][0]);
-    a = __builtin_fmaxf(__builtin_fmaxf(a, s[1][nt][1]), s[1][nt][2]);
-    mloc[nt] = __builtin_fmaxf(a, s[1][nt][3]);
-    need |= mloc[nt] > st.m[nt] + kTau;
-  }
-  if (!__builtin_amdgcn_ballot_w64(need)) return false;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const float mrow = group4_max(mloc[nt]);
-    const bool up = mrow > st.m[nt] + kTau;
-    alpha[nt] = up ? __builtin_amdgcn_exp2f((st.m[nt] - mrow) * kLog2e) : 1.0f;
-    st.m[nt] = up ? mrow : st.m[nt];
-    st.l[nt] *= alpha[nt];
-  }
-  return true;
-}
-
-__device__ inline void copy_scores(const f32x4 (&from)[2][4], f32x4 (&to)[2][4]) {
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) to[mt][nt] = from[mt][nt];
 }
 
 // Scheduling hints: interleave `nmfma` MFMAs with `per` VALU instructions each.
@@ -475,206 +352,368 @@ __device__ inline void copy_scores(const f32x4 (&from)[2][4], f32x4 (&to)[2][4])
     }                                                            \
   } while (0)
 
+__device__ inline float tree_max16(const f32x16 &v) {
+  const float a0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+  const float a1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+  const float a2 = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+  const float a3 = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+  const float a4 = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+  const float b0 = __builtin_fmaxf(__builtin_fmaxf(a0, a1), a2);
+  const float b1 = __builtin_fmaxf(__builtin_fmaxf(a3, a4), v[15]);
+  return __builtin_fmaxf(b0, b1);
+}
+
+// Value of the other half of the wavefront (lane l ^ 32).
+__device__ inline float swap_halves(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const int lane = (int)__builtin_amdgcn_workitem_id_x();
+  return __uint_as_float(lane < 32 ? a[1] : a[0]);
+}
+
+// CINIT: subtract the reference max through the MFMA accumulator input (costs
+// 32 registers); otherwise one v_sub per score.
+#ifndef BBSA_CINIT
+#define BBSA_CINIT 0
+#endif
 template <bool HAS_MASK>
 __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
+  constexpr bool CINIT = BBSA_CINIT;
+  const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x());
+  if (it.bh >= p.bh_total) return;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kTileBytes];
-  unsigned char *const kbuf = lds;                    // K tiles: kbuf + (i & 1) * kTileBytes
+  unsigned char *const kbuf = lds;                    // K tile i at kbuf + (i & 1) * kTileBytes
   unsigned char *const vbuf = lds + 2 * kTileBytes;   // V tiles
-  const int lane = (int)__builtin_amdgcn_workitem_id_x(), c = lane & 15, g = lane >> 4;
-  const int home = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7);  // HW_REG_XCC_ID
 
-  // Static assignment: wavefront w serves XCD class w % 8 (the XCD it runs
-  // on) and takes that class's items w/8, w/8 + W, w/8 + 2W, ... with W the
-  // number of wavefronts of the class.
-  const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-  const int cls = wg & 7;
-  const int stride = (p.n_waves - cls + 7) / 8;
-  const int n_cls = class_items(p, cls);
-  int kidx = wg >> 3;
-  if (kidx >= n_cls) return;
-  (void)home;
+  const int lane = (int)__builtin_amdgcn_workitem_id_x();
+  const int c = lane & 31, h = lane >> 5;             // MFMA 32x32 lane coordinates
+  const int G = lane >> 4, cc = lane & 15;            // 16-lane groups of the transposed reads
+  const int b = it.bh / p.H;
+  const bf16_t *Kbh = (const bf16_t *)p.k + (int64_t)it.bh * p.seq_stride;
+  const bf16_t *Vbh = (const bf16_t *)p.v + (int64_t)it.bh * p.seq_stride;
+  const float *mrow = HAS_MASK ? p.mask + (int64_t)b * p.L : nullptr;
+  const int q0 = it.qblock * p.block + it.qt * kQT;
 
-  // DMA sources (element offsets inside a 32-key step).  Row of instruction u
-  // is 8u + lane/8; K's swizzle flips with the parity of u, V's does not.
+  // DMA sources inside a 32-key step (elements): instruction u loads key row
+  // 8u + lane/8, chunk (lane % 8) ^ f(row).
   const int drow = lane >> 3;
-  const int kcol_even = 8 * ((lane & 7) ^ drow);
-  const int kcol_odd = 8 * ((lane & 7) ^ drow ^ 1);
-  const int vcol = 8 * ((lane & 7) ^ v_swz(drow));
-  // LDS read offsets.  K A-operand: row 16mt + c, chunk 4s + g.
-  int koff[2];
+  int kdma[4];
 #pragma unroll
-  for (int ss = 0; ss < 2; ++ss) koff[ss] = c * 128 + 16 * ((4 * ss + g) ^ k_swz(c));
-  // V^T transposed reads: key row 16mt + 4g + c/4, d = 16dt + 4(c%4) .. +3.
-  int voff[4];
+  for (int u = 0; u < 4; ++u) kdma[u] = (8 * u + drow) * kD + 8 * ((lane & 7) ^ k_swz(8 * u + drow));
+  const int vdma = drow * kD + 8 * ((lane & 7) ^ v_swz(drow));   // v_swz(8u + drow) == v_swz(drow)
+  // K A-operand reads, k-step k: row c, chunk 2k + h.
+  int koff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = c * 128 + 16 * ((2 * kk + h) ^ k_swz(c));
+  // V^T transposed reads for d-tile dt, key step s, run r: the lane reads key row
+  // 16s + 8r + 4(G/2) + cc/4, d = 32dt + 16(G%2) + 4(cc%4) .. +3.
+  int voff[2];
   {
-    const int row = 4 * g + (c >> 2), qq = c & 3;
+    const int row = 4 * (G >> 1) + (cc >> 2);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      voff[dt] = row * 128 + 16 * ((2 * dt + (qq >> 1)) ^ v_swz(row)) + 8 * (qq & 1);
+    for (int dt = 0; dt < 2; ++dt) {
+      const int chunk = 4 * dt + 2 * (G & 1) + ((cc & 3) >> 1);
+      voff[dt] = row * 128 + 16 * (chunk ^ v_swz(row)) + 8 * (cc & 1);
+    }
   }
 
-  auto dma_k = [&](int bh, int key0, int slot) {
-    const bf16_t *kb = (const bf16_t *)p.k + (int64_t)bh * p.seq_stride + (int64_t)(key0 + drow) * kD;
+  // Q^T operand: lane (c, h) holds Q[q0 + 32nt + c][16k + 8h .. +7]; with
+  // CINIT the values are pre-scaled by log2(e) (rounded to bf16) so that the
+  // MFMA accumulates scores in log2 units.
+  bf16x8 qf[2][4];
+  {
+    const bf16_t *Q = (const bf16_t *)p.q + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 raw = *(const bf16x8 *)(Q + (int64_t)(32 * nt + c) * kD + 16 * kk + 8 * h);
+        if (CINIT) {
+          typedef float f32x8 __attribute__((ext_vector_type(8)));
+          const f32x8 f = __builtin_convertvector(raw, f32x8) * kLog2e;
+          qf[nt][kk] = __builtin_convertvector(f, bf16x8);
+        } else {
+          qf[nt][kk] = raw;
+        }
+      }
+  }
+
+  const KeyWalk walk = make_walk(p, it);
+  const int n = walk.n_steps;                 // >= 2
+  WalkCursor ck, cv;                          // K runs two steps ahead of V
+  ck.start(p, walk);
+  cv.start(p, walk);
+
+  auto dma_k = [&](int key0, int slot) {
+    const bf16_t *src = Kbh + (int64_t)key0 * kD;
     unsigned char *dst = kbuf + slot * kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(kb + u * 8 * kD + ((u & 1) ? kcol_odd : kcol_even), dst + 1024 * u);
+    for (int u = 0; u < 4; ++u) dma16(src + kdma[u], dst + 1024 * u);
   };
-  auto dma_v = [&](int bh, int key0, int slot) {
-    const bf16_t *vb = (const bf16_t *)p.v + (int64_t)bh * p.seq_stride + (int64_t)(key0 + drow) * kD;
+  auto dma_v = [&](int key0, int slot) {
+    const bf16_t *src = Vbh + (int64_t)key0 * kD;
     unsigned char *dst = vbuf + slot * kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(vb + u * 8 * kD + vcol, dst + 1024 * u);
+    for (int u = 0; u < 4; ++u) dma16(src + 8 * u * kD + vdma, dst + 1024 * u);
   };
-  auto load_mask = [&](int bh, int key0, f32x4 (&mk)[2]) {
-    const float *mrow = p.mask + (int64_t)(bh / p.H) * p.L + key0;
-    mk[0] = *(const f32x4 *)(mrow + 4 * g);
-    mk[1] = *(const f32x4 *)(mrow + 16 + 4 * g);
-  };
-  auto read_k = [&](int slot, bf16x8 (&kc)[2][2]) {
+  // Mask value of key key0 + lane % 32 (one float per lane, lanes l and l + 32 equal).
+  auto load_mask = [&](int key0) -> float { return HAS_MASK ? mrow[key0 + c] : 1.0f; };
+  auto read_k = [&](int slot, bf16x8 (&kc)[4]) {
     const unsigned char *src = kbuf + slot * kTileBytes;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) kc[mt][ss] = *(const bf16x8 *)(src + koff[ss] + 2048 * mt);
+    for (int kk = 0; kk < 4; ++kk) kc[kk] = *(const bf16x8 *)(src + koff[kk]);
   };
-  auto read_vt = [&](int slot, bf16x8 (&vt)[4]) {
+  auto read_vt = [&](int slot, bf16x8 (&vt)[2][2]) {
     const unsigned char *src = vbuf + slot * kTileBytes;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + voff[dt]));
-      const s16x4 bb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + voff[dt] + 2048));
-      vt[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  };
-  bf16x8 qf[4][2];
-  // Q^T operand: lane (c, g) holds Q[q0 + 16nt + c][32s + 8g .. +7].
-  auto load_q = [&](const Item &it) {
-    const bf16_t *Q = (const bf16_t *)p.q + (int64_t)it.bh * p.seq_stride +
-                      (int64_t)(it.qblock * p.block + it.qt * kQT) * kD;
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss)
-        qf[nt][ss] = *(const bf16x8 *)(Q + (int64_t)(16 * nt + c) * kD + 32 * ss + 8 * g);
-  };
-  auto scores = [&](const bf16x8 (&kc)[2][2], f32x4 (&sc)[2][4]) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[mt][0], qf[nt][0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[mt][1], qf[nt][1], acc, 0, 0, 0);
-        sc[mt][nt] = acc;
+      for (int s = 0; s < 2; ++s) {
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + voff[dt] + 2048 * s));
+        const s16x4 bb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + voff[dt] + 2048 * s + 1024));
+        vt[dt][s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, 6, 7));
       }
   };
 
-  SoftmaxState st;
-  f32x4 o[4][4];
-  Item it = item_from_ticket(p, kidx * 8 + cls);
+  // Online softmax state (log2 units).  mref: reference max of each of the
+  // lane's two query columns (equal in lanes c and c + 32); initc: -mref
+  // broadcast, the accumulator input of the score MFMAs; l: lane-partial sums.
+  float mref[2] = {0.0f, 0.0f}, l[2] = {0.0f, 0.0f};
+  f32x16 initc[CINIT ? 2 : 1];
+#pragma unroll
+  for (int nt = 0; nt < (CINIT ? 2 : 1); ++nt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) initc[nt][e] = 0.0f;
+  f32x16 o[2][2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][nt][e] = 0.0f;
 
-  for (;;) {
-    const KeyWalk walk = make_walk(p, it);
-    const int n = walk.n_steps;           // >= 2
-    WalkCursor ck, cv;                    // K runs two steps ahead of V
-    ck.start(p, walk);
-    cv.start(p, walk);
+  // S(j) = K Q^T - mref for 32 keys x 64 queries (log2 units).
+  auto scores = [&](const bf16x8 (&kc)[4], f32x16 (&sc)[2]) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) { st.m[nt] = kInitMax; st.l[nt] = 0.0f; }
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x16 acc;
+      if (CINIT) {
+        acc = initc[nt];
+      } else {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+      }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[kk], qf[nt][kk], acc, 0, 0, 0);
+      sc[nt] = acc;
+    }
+  };
+  // Padding bias for the step whose lane value is mval: nothing when every key
+  // is valid, one scalar when all 32 keys share a mask value, per key otherwise.
+  auto apply_mask = [&](f32x16 (&sc)[2], float mval) {
+    if (!HAS_MASK) return;
+    const unsigned long long pad = __builtin_amdgcn_ballot_w64(mval != 1.0f);
+    if (!pad) return;
+    const float m0 = __builtin_amdgcn_readfirstlane(mval);
+    const float bl = CINIT ? kPadBias * kLog2e : kPadBias;
+    if (!__builtin_amdgcn_ballot_w64(mval != m0)) {
+      const float bias = bl * (1.0f - m0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sc[nt] += bias;
+      return;
+    }
+    // Per key: register 4j + i holds key 8j + 4h + i, whose mask sits in lane 8j + 4h + i.
+    f32x16 bias;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+      bias[e] = bl * (1.0f - __uint_as_float(__builtin_amdgcn_ds_bpermute(key * 4, __float_as_uint(mval))));
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) sc[nt] += bias;
+  };
 
-    // Prologue: K(0), K(1), Q; S(0).
-    f32x4 mk[2];
-    if (HAS_MASK) load_mask(it.bh, ck.key0, mk);
-    dma_k(it.bh, ck.key0, 0);
-    load_q(it);
-    ck.advance(p, walk);
-    dma_k(it.bh, ck.key0, 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    f32x4 sA[2][4], sB[2][4];
+  // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
+  // bias is added at the top of the iteration that takes its softmax.
+  float mk_cur = load_mask(ck.key0);          // mask of step j (j = 0)
+  dma_k(ck.key0, 0);
+  ck.advance(p, walk);
+  float mk_next = load_mask(ck.key0);         // mask of step j + 1
+  dma_k(ck.key0, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  f32x16 sA[2], sB[2];
+  {
+    bf16x8 kc[4];
+    read_k(0, kc);
+    scores(kc, sA);
+  }
+
+  bf16x8 pf[2][2];    // P of the previous step: [nt][key step s]
+  bool resc_pending = false;
+  float alpha_pending[2] = {1.0f, 1.0f};
+  // One pipeline iteration j: softmax of step j (in s_cur), S(j+1) into
+  // s_next, PV of step j-1.
+  auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    constexpr bool HAS_S = decltype(has_s_t)::value;
+    constexpr bool HAS_PV = decltype(has_pv_t)::value;
+    constexpr bool FIRST = decltype(first_t)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K(j+1), V(j-1), mask(j+2) from iteration j-1
+    bf16x8 kc[4], vt[2][2];
+    if (HAS_S) read_k((j + 1) & 1, kc);
+    if (HAS_PV) read_vt((j - 1) & 1, vt);
+    apply_mask(s_cur, mk_cur);
+    float mk_n2 = 1.0f;
+    if (j + 2 < n) {
+      ck.advance(p, walk);
+      mk_n2 = load_mask(ck.key0);
+      dma_k(ck.key0, j & 1);
+    }
+    dma_v(cv.key0, j & 1);
+    cv.advance(p, walk);
+
+    // A rescale decided in the previous iteration applies to O now: after the
+    // PV product of step j-2 and before that of step j-1 (whose probabilities
+    // already use the new reference).
+    if (resc_pending) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha_pending[nt];
+      resc_pending = false;
+    }
+    // Rescale decision for step j (before its exponentials).
     {
-      bf16x8 kc[2][2];
-      read_k(0, kc);
-      scores(kc, sA);
-      if (HAS_MASK) apply_mask(sA, mk);
+      // Scores relative to the reference max (log2 units).
+      float ml[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        ml[nt] = CINIT ? tree_max16(s_cur[nt]) : tree_max16(s_cur[nt]) * kLog2e - mref[nt];
+      const bool need = FIRST || ml[0] > kTauLog2 || ml[1] > kTauLog2;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const float mrow = __builtin_fmaxf(ml[nt], swap_halves(ml[nt]));
+          const float sh = (FIRST || mrow > kTauLog2) ? mrow : 0.0f;
+          mref[nt] += sh;
+          if (CINIT) {
+            s_cur[nt] -= sh;
+            initc[CINIT ? nt : 0] -= sh;
+          }
+          alpha_pending[nt] = __builtin_amdgcn_exp2f(-sh);
+          if (!FIRST) l[nt] *= alpha_pending[nt];
+        }
+        // The first step has no O to rescale.
+        resc_pending = !FIRST;
+      }
     }
 
-    bf16x8 pf[4];       // P of the previous step
-    // One pipeline iteration j.  HAS_S: S(j+1) exists; HAS_PV: step j-1 exists.
-    // s_cur holds S(j) (softmaxed here); S(j+1) is written to s_next.
-    auto iteration = [&](int j, auto has_s_t, auto has_pv_t, f32x4 (&s_cur)[2][4], f32x4 (&s_next)[2][4]) {
-      constexpr bool HAS_S = decltype(has_s_t)::value;
-      constexpr bool HAS_PV = decltype(has_pv_t)::value;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K(j+1), V(j-1), mask(j+1)
-      bf16x8 kc[2][2], vt[4];
-      if (HAS_S) read_k((j + 1) & 1, kc);
-      if (HAS_PV) read_vt((j - 1) & 1, vt);
-      f32x4 mk_next[2];
-      if (HAS_S && HAS_MASK) load_mask(it.bh, ck.key0, mk_next);
-      if (j + 2 < n) {
-        ck.advance(p, walk);
-        dma_k(it.bh, ck.key0, j & 1);
-      }
-      dma_v(it.bh, cv.key0, j & 1);
-      cv.advance(p, walk);
-
-      float alpha[4];
-      const bool resc = rescale_decide(s_cur, st, alpha);
-
-      if (HAS_S) scores(kc, s_next);
-      if (HAS_PV) {
+    if (HAS_S) scores(kc, s_next);
+    if (HAS_PV) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[dt], pf[nt], o[dt][nt], 0, 0, 0);
-      }
-      softmax_exp(s_cur, st);
-      // P^T operand: key order (mt, i) matches the V^T operand's k slots.
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bf16x4 lo = __builtin_convertvector(s_cur[0][nt], bf16x4);
-        const bf16x4 hi = __builtin_convertvector(s_cur[1][nt], bf16x4);
-        pf[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      row_sum_bf16(pf, st);
-      if (HAS_S && HAS_PV) BBSA_INTERLEAVE(32, 3);
-      else BBSA_INTERLEAVE(16, 6);
-      if (resc) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) o[dt][nt] *= alpha[nt];
-      }
-      if (HAS_S && HAS_MASK) apply_mask(s_next, mk_next);
-    };
-
-    using T = std::true_type;
-    using F = std::false_type;
-    iteration(0, T{}, F{}, sA, sB);
-    copy_scores(sB, sA);
-    for (int j = 1; j < n - 1; ++j) {
-      iteration(j, T{}, T{}, sA, sB);
-      copy_scores(sB, sA);
+          for (int s = 0; s < 2; ++s)
+            o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
     }
-    iteration(n - 1, F{}, T{}, sA, sB);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // V(n-1)
-    {
-      bf16x8 vt[4];
-      read_vt((n - 1) & 1, vt);
+    // Softmax of step j: p = 2^(s - mref), rounded to bf16 for the PV product;
+    // the row sums add the rounded values (the ones the product uses).
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+    for (int nt = 0; nt < 2; ++nt) {
+      const float nm = CINIT ? 0.0f : mref[nt];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[dt], pf[nt], o[dt][nt], 0, 0, 0);
+      for (int e = 0; e < 16; ++e)
+        s_cur[nt][e] = __builtin_amdgcn_exp2f(CINIT ? s_cur[nt][e] : __builtin_fmaf(s_cur[nt][e], kLog2e, -nm));
+      float part[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 lo = {s_cur[nt][8 * s + 0], s_cur[nt][8 * s + 1], s_cur[nt][8 * s + 2], s_cur[nt][8 * s + 3]};
+        const f32x4 hi = {s_cur[nt][8 * s + 4], s_cur[nt][8 * s + 5], s_cur[nt][8 * s + 6], s_cur[nt][8 * s + 7]};
+        pf[nt][s] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+        float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 0, 1), ones, 0.0f, false);
+        float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 2, 3), ones, 0.0f, false);
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 4, 5), ones, a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 6, 7), ones, a1, false);
+        part[s] = a0 + a1;
+      }
+      l[nt] += part[0] + part[1];
     }
-    finish_item<bf16_t>(p, it, it.qblock * p.block + it.qt * kQT, st, o);
-    kidx += stride;
-    if (kidx >= n_cls) break;
-    it = item_from_ticket(p, kidx * 8 + cls);
+    if (HAS_S && HAS_PV) BBSA_INTERLEAVE(16, 6);
+    else BBSA_INTERLEAVE(8, 10);
+    mk_cur = mk_next;
+    mk_next = mk_n2;
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  iteration(0, T{}, F{}, T{}, sA, sB);
+  sA[0] = sB[0];
+  sA[1] = sB[1];
+  for (int j = 1; j < n - 1; ++j) {
+    iteration(j, T{}, T{}, F{}, sA, sB);
+    sA[0] = sB[0];
+    sA[1] = sB[1];
+  }
+  iteration(n - 1, F{}, T{}, F{}, sA, sB);
+  // Drain: PV of the last step.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (resc_pending) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha_pending[nt];
+  }
+  {
+    bf16x8 vt[2][2];
+    read_vt((n - 1) & 1, vt);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
+  }
+
+  // Finish: full row sums, then normalised bf16 output or a split-K partial.
+  float lsum[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) lsum[nt] = l[nt] + swap_halves(l[nt]);
+  if (it.grow >= 0 && p.chunks > 1) {
+    const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.chunks + it.chunk;
+    float *part = p.ws + pidx * kPartialFloats;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 y = {o[dt][nt][4 * jj], o[dt][nt][4 * jj + 1], o[dt][nt][4 * jj + 2], o[dt][nt][4 * jj + 3]};
+          *(f32x4 *)(part + (32 * nt + c) * kD + 32 * dt + 8 * jj + 4 * h) = y;
+        }
+    if (h == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        part[kQT * kD + 32 * nt + c] = mref[nt];
+        part[kQT * kD + kQT + 32 * nt + c] = lsum[nt];
+      }
+    }
+    return;
+  }
+  bf16_t *out = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float inv = 1.0f / lsum[nt];
+    bf16_t *row = out + (int64_t)(32 * nt + c) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 y = {o[dt][nt][4 * jj], o[dt][nt][4 * jj + 1], o[dt][nt][4 * jj + 2], o[dt][nt][4 * jj + 3]};
+        *(bf16x4 *)(row + 32 * dt + 8 * jj + 4 * h) = __builtin_convertvector(y * inv, bf16x4);
+      }
   }
 }
 
@@ -767,43 +806,42 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
 
 // ---------------------------------------------------------------- split-K merge
 //
-// One 64-thread workgroup per (batch, head, full row, query tile, 16-query
-// slice); thread t handles query 16 * slice + t / 4 and 16 consecutive d.
-// out = sum_c w_c O_c / sum_c w_c l_c with w_c = 2^((m_c - M) log2 e),
-// M = max_c m_c.
+// One 64-thread workgroup per (batch, head, full row, query tile, 4-query
+// slice); 16 threads per query, each owning 4 consecutive d.  First the
+// maximum M of the chunks' reference maxima, then out = sum_c w_c O_c /
+// sum_c w_c l_c with w_c = 2^(m_c - M) (maxima in log2 units).
+constexpr int kMergeSlices = kQT / 4;
 template <typename OutT>
 __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-  const int slice = wg & 3, idx = wg >> 2;
+  const int slice = wg % kMergeSlices, idx = wg / kMergeSlices;
   const int qt = idx % p.qtiles;
   const int t2 = idx / p.qtiles;
   const int grow = t2 % p.n_rows_global;
   const int bh = t2 / p.n_rows_global;
   const float *base = p.ws + (int64_t)idx * p.chunks * kPartialFloats;
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
-  const int q = 16 * slice + (tid >> 2), dq = tid & 3;
+  const int q = 4 * slice + (tid >> 4), dq = tid & 15;
+  const int nch = p.chunks;
   float M = kInitMax;
-  for (int ch = 0; ch < p.chunks; ++ch) M = __builtin_fmaxf(M, base[(int64_t)ch * kPartialFloats + kQT * kD + q]);
+#pragma unroll 4
+  for (int ch = 0; ch < nch; ++ch) M = __builtin_fmaxf(M, base[(int64_t)ch * kPartialFloats + kQT * kD + q]);
   float den = 0.0f;
-  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int ch = 0; ch < p.chunks; ++ch) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int ch = 0; ch < nch; ++ch) {
     const float *part = base + (int64_t)ch * kPartialFloats;
-    const float w = __builtin_amdgcn_exp2f((part[kQT * kD + q] - M) * kLog2e);
+    const float w = __builtin_amdgcn_exp2f(part[kQT * kD + q] - M);
     den += w * part[kQT * kD + kQT + q];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += w * *(const f32x4 *)(part + q * kD + 16 * dq + 4 * e);
+    acc += w * *(const f32x4 *)(part + q * kD + 4 * dq);
   }
-  const float inv = 1.0f / den;
+  const f32x4 y = acc * (1.0f / den);
   const int qblock = (p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow;
-  OutT *row = (OutT *)p.out + (int64_t)bh * p.seq_stride + (int64_t)(qblock * p.block + qt * kQT + q) * kD + 16 * dq;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f32x4 y = acc[e] * inv;
-    if constexpr (sizeof(OutT) == 2) {
-      *(bf16x4 *)(row + 4 * e) = __builtin_convertvector(y, bf16x4);
-    } else {
-      *(f32x4 *)(row + 4 * e) = y;
-    }
+  OutT *row = (OutT *)p.out + (int64_t)bh * p.seq_stride + (int64_t)(qblock * p.block + qt * kQT + q) * kD + 4 * dq;
+  if constexpr (sizeof(OutT) == 2) {
+    *(bf16x4 *)row = __builtin_convertvector(y, bf16x4);
+  } else {
+    *(f32x4 *)row = y;
   }
 }
 
@@ -812,8 +850,6 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
 struct DeviceWorkspace {
   void *ptr = nullptr;       // split-K partials
   size_t bytes = 0;
-  int *ctrl = nullptr;       // work-queue control block, zero between calls
-  int waves[2] = {0, 0};     // persistent wavefronts of bbsa_attn_bf16<false/true>
 };
 
 std::mutex g_mutex;
@@ -829,33 +865,14 @@ struct Timing {
 };
 Timing g_timing;
 
-// Per-device state for one call: the control block and the persistent grid
-// size of the bf16 kernel (created on first use), and the partials buffer.
-int device_state(size_t bytes, bool masked, float **ws, int **ctrl, int *waves) {
+// Library-owned split-K workspace of the current device, grown on demand.
+int ensure_workspace(size_t bytes, float **ws) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return BBSA_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_mutex);
   if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
   DeviceWorkspace &w = g_ws[dev];
-  if (!w.ctrl) {
-    int cus = 0, occ0 = 0, occ1 = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return BBSA_ERR_HIP;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ0, (const void *)bbsa_attn_bf16<false>, 64, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, (const void *)bbsa_attn_bf16<true>, 64, 0) != hipSuccess)
-      return BBSA_ERR_HIP;
-    int *c = nullptr;
-    if (hipMalloc(&c, kCtrlInts * sizeof(int)) != hipSuccess) return BBSA_ERR_HIP;
-    if (hipMemset(c, 0, kCtrlInts * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      (void)hipFree(c);
-      return BBSA_ERR_HIP;
-    }
-    w.ctrl = c;
-    w.waves[0] = (occ0 > 0 ? occ0 : 1) * cus;
-    w.waves[1] = (occ1 > 0 ? occ1 : 1) * cus;
-  }
-  *ctrl = w.ctrl;
-  *waves = w.waves[masked ? 1 : 0];
-  if (bytes > 0 && w.bytes < bytes) {
+  if (w.bytes < bytes) {
     if (w.ptr) {
       if (hipDeviceSynchronize() != hipSuccess) return BBSA_ERR_HIP;
       if (hipFree(w.ptr) != hipSuccess) return BBSA_ERR_HIP;
@@ -906,31 +923,23 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   const int64_t grid = p.xcd_remap ? 8 * ((bh + 7) / 8) * items_per_bh : bh * items_per_bh;
   const int64_t n_partials = (p.chunks > 1) ? bh * p.n_rows_global * p.qtiles * p.chunks : 0;
   if (grid > 0x7fffffff || bh > 0x7fffffff || (int64_t)B * H * L * kD > ((int64_t)1 << 40) ||
-      bh * p.n_rows_global * p.qtiles > 0x7fffffff)
+      (int64_t)kMergeSlices * bh * p.n_rows_global * p.qtiles > 0x7fffffff)
     return BBSA_ERR_UNSUPPORTED;
   p.items_per_bh = (int)items_per_bh;
   p.bh_total = (int)bh;
-
-  int waves = 0;
-  {
-    const int rc = device_state((size_t)n_partials * kPartialFloats * sizeof(float), mask != nullptr,
-                                &p.ws, &p.ctrl, &waves);
+  if (n_partials > 0) {
+    const int rc = ensure_workspace((size_t)n_partials * kPartialFloats * sizeof(float), &p.ws);
     if (rc != BBSA_OK) return rc;
   }
-  const int64_t total_items = bh * items_per_bh;
-  p.n_waves = (int)(total_items < waves ? total_items : waves);
-  if (p.n_waves < 8) p.n_waves = 8;   // every XCD class gets a wavefront
 
   const bool timed = g_timing.enabled && g_timing.n < kMaxTimed;
   const int tslot = g_timing.n;
   if (timed && hipEventRecord(g_timing.ev[tslot][0], stream) != hipSuccess) return BBSA_ERR_HIP;
-  const dim3 b1(64);
+  const dim3 g1((unsigned)grid), b1(64);
   if (dtype == BBSA_BF16) {
-    const dim3 g1((unsigned)p.n_waves);
     if (mask) hipLaunchKernelGGL(bbsa_attn_bf16<true>, g1, b1, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_attn_bf16<false>, g1, b1, 0, stream, p);
   } else {
-    const dim3 g1((unsigned)grid);
     if (mask) hipLaunchKernelGGL(bbsa_attn_f32<true>, g1, b1, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_attn_f32<false>, g1, b1, 0, stream, p);
   }
@@ -938,7 +947,7 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   if (timed && hipEventRecord(g_timing.ev[tslot][1], stream) != hipSuccess) return BBSA_ERR_HIP;
   if (n_partials > 0) {
     if (timed && hipEventRecord(g_timing.ev[tslot][2], stream) != hipSuccess) return BBSA_ERR_HIP;
-    const dim3 g2((unsigned)(4 * bh * p.n_rows_global * p.qtiles)), b2(64);
+    const dim3 g2((unsigned)(kMergeSlices * bh * p.n_rows_global * p.qtiles)), b2(64);
     if (dtype == BBSA_BF16) hipLaunchKernelGGL(bbsa_combine<bf16_t>, g2, b2, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_combine<float>, g2, b2, 0, stream, p);
     if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
@@ -970,11 +979,10 @@ extern "C" void bbsa_release_workspace(void) {
   if (hipGetDevice(&cur) != hipSuccess) return;
   for (size_t dev = 0; dev < g_ws.size(); ++dev) {
     DeviceWorkspace &w = g_ws[dev];
-    if (!w.ptr && !w.ctrl) continue;
+    if (!w.ptr) continue;
     if (hipSetDevice((int)dev) == hipSuccess) {
       (void)hipDeviceSynchronize();
-      if (w.ptr) (void)hipFree(w.ptr);
-      if (w.ctrl) (void)hipFree(w.ctrl);
+      (void)hipFree(w.ptr);
     }
     w = DeviceWorkspace();
   }
