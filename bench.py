@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -115,6 +117,17 @@ def main():
 
     import torch
     from block_sparse_long_bbsa_amd import bbsa, workloads
+
+    if args.copy_calibration:
+        # A plain copy of known size: 256 MiB read + 256 MiB written per dispatch.
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
+        return
 
     w = workloads.WORKLOADS[args.workload]
     elt = 2 if w.dtype == "bf16" else 4
