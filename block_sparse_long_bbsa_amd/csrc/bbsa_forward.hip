@@ -13,10 +13,10 @@
 //     block and walks the item's key blocks in steps of 32 keys;
 //   * bf16 path: scores are computed transposed, S^T = K Q^T, on MFMA
 //     32x32x16 bf16, so each lane holds 16 keys of one query column and the
-//     row max needs a single cross-lane swap; Q is pre-scaled by log2(e) and
-//     the running reference max is subtracted for free by feeding a broadcast
-//     (-max) tuple as the MFMA accumulator input, so a probability costs one
-//     v_exp_f32;
+//     row max needs a single cross-lane swap; a probability costs one FMA
+//     (score * log2(e) - reference max) and one v_exp_f32 (the BBSA_CINIT
+//     build option instead folds both into a log2(e)-scaled Q and the MFMA
+//     accumulator input);
 //   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
 //     XOR-swizzled rows); K is read back as the MFMA A operand, V is read back
 //     transposed with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T;

@@ -106,6 +106,10 @@ int bbsa_check_rand_attn(const int32_t *rand_attn, int H, int nb, int r);
  * stream:    HIP stream; kernels are enqueued on it, no host synchronisation.
  * dtype:     BBSA_BF16 (fp32 accumulation, bf16 output) or BBSA_F32.
  *
+ * Limits (BBSA_ERR_UNSUPPORTED beyond them): d = 64; block 64 or 128;
+ * on the sparse path 5 + r <= 64 (a middle row attends at most 64 key
+ * blocks); B * H * L * d <= 2^40 elements; at most 2^31 - 1 workgroups.
+ *
  * Returns BBSA_OK, or BBSA_OK_FULL_FALLBACK when L <= (5 + 2r) * block (every
  * query block then attends every key block), or a negative error code.  All
  * argument checks happen before any HIP call.  The library-owned workspace is

@@ -28,7 +28,7 @@ Sources (by page title and section):
   ``(5 + 2*num_random_blocks) * block_size`` the layer falls back to full
   attention.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * no internal softmax scale -- the caller folds 1/sqrt(d) into Q;
 * padding is key-side only: bias ``-10000 * (1 - mask[key])`` on every
