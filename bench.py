@@ -107,8 +107,10 @@ def cpu_baseline(inp, plan, w, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # The GPU's clocks take tens of milliseconds of sustained work to ramp up;
+    # the default warm-up (about 0.15 s of work at L=4096) covers that.
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
@@ -171,7 +173,7 @@ def main():
 
     # Same steps again with the library's own HIP events around each kernel.
     bbsa.bbsa_timing_enable(True)
-    for i in range(args.steps):
+    for i in range(min(args.steps, 4096)):
         step(i)
     torch.cuda.synchronize()
     main_ms, comb_ms, calls = bbsa.bbsa_timing_read()

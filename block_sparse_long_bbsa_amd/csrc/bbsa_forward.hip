@@ -41,6 +41,7 @@
 
 #include "bbsa.h"
 
+
 namespace {
 
 typedef __bf16 bf16_t;
@@ -94,21 +95,23 @@ struct Item {
   int chunk;      // key chunk of a full row
 };
 
-// Workgroup -> item.  Items of one (batch, head) are numbered full-row chunks
-// first (the longest items start first), then middle rows in order.  With the
-// XCD remap, workgroup w runs on XCD w % 8 and takes the (w / 8)-th item of
-// the (batch, head) pairs x, x + 8, x + 16, ... (x = w % 8), so all items of
-// one pair share one L2.
+// Workgroup -> item.  Workgroups are dispatched in index order, so the
+// longest items (full-row chunks) of every (batch, head) come first and the
+// middle rows fill in behind them; this keeps long items out of the tail.
+// With the XCD remap, workgroup w runs on XCD x = w % 8 and serves only the
+// (batch, head) pairs x, x + 8, x + 16, ..., so all items of one pair share
+// one L2.
 __device__ inline Item decode_item(const Params &p, int wg) {
-  int bh, local;
-  if (p.xcd_remap) {
-    const int xcd = wg & 7, slot = wg >> 3;
-    bh = xcd + 8 * (slot / p.items_per_bh);
-    local = slot % p.items_per_bh;
-  } else {
-    bh = wg / p.items_per_bh;
-    local = wg % p.items_per_bh;
-  }
+  const int lanes = p.xcd_remap ? 8 : 1;
+  const int x = p.xcd_remap ? (wg & 7) : 0, slot = p.xcd_remap ? (wg >> 3) : wg;
+  const int per_x = (p.bh_total + lanes - 1) / lanes;     // pairs served per XCD
+  const int n_glob = per_x * p.n_global_items;
+  const int n_mid = max(p.items_per_bh - p.n_global_items, 1);
+  const bool g = slot < n_glob;
+  const int s2 = slot - n_glob;
+  const int j = g ? slot / p.n_global_items : s2 / n_mid;
+  const int local = g ? slot % p.n_global_items : p.n_global_items + s2 % n_mid;
+  const int bh = x + lanes * j;
   const bool global_row = local < p.n_global_items;
   const int per_row = p.qtiles * p.chunks;
   const int m = local - p.n_global_items;
@@ -229,6 +232,7 @@ struct KeyWalk {
   int n_steps;
   int steps_per_block;
   int blk;             // per lane: key block at list position `lane`
+  int first_blk;       // the block at position 0 (uniform)
 };
 
 struct WalkCursor {
@@ -236,7 +240,7 @@ struct WalkCursor {
   __device__ inline void start(const Params &p, const KeyWalk &w) {
     t = 0;
     sb = 0;
-    key0 = __builtin_amdgcn_readfirstlane(w.blk) * p.block;
+    key0 = w.first_blk * p.block;   // uniform: does not wait for the plan load
   }
   __device__ inline void advance(const Params &p, const KeyWalk &w) {
     if (++sb == w.steps_per_block) {
@@ -260,6 +264,7 @@ __device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
   const int first = it.chunk * p.chunk_blocks;
   const int nblk = middle ? 2 + nw + p.r : min(p.chunk_blocks, p.nb - first);
   w.n_steps = __builtin_amdgcn_readfirstlane(nblk * w.steps_per_block);
+  w.first_blk = middle ? 0 : first;
   int blk;
   if (middle) {
     // Middle query block i: the two global blocks, the window without them,
@@ -338,6 +343,8 @@ __device__ inline int v_swz(int row) { return ((row >> 1) & 1) << 2; }
 
 typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle, no stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ inline void dma16(const void *src, unsigned char *lds_dst) {
   __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_dst, 16, 0, 0);
@@ -443,17 +450,28 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   ck.start(p, walk);
   cv.start(p, walk);
 
+  // K and V of this (batch, head) as buffer resources: the DMA source of a
+  // lane is a 32-bit per-lane offset plus a scalar offset for the step, and
+  // the hardware range check keeps every read inside the pair's L x d rows.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Kbh, (short)0, p.L * kD * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Vbh, (short)0, p.L * kD * 2, kBufferWord3);
+  int kdma_b[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kdma_b[u] = 2 * kdma[u];
+  const int vdma_b = 2 * vdma;
   auto dma_k = [&](int key0, int slot) {
-    const bf16_t *src = Kbh + (int64_t)key0 * kD;
     unsigned char *dst = kbuf + slot * kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(src + kdma[u], dst + 1024 * u);
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)(dst + 1024 * u), 16, kdma_b[u], key0 * (kD * 2), 0, 0);
   };
   auto dma_v = [&](int key0, int slot) {
-    const bf16_t *src = Vbh + (int64_t)key0 * kD;
     unsigned char *dst = vbuf + slot * kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(src + 8 * u * kD + vdma, dst + 1024 * u);
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)(dst + 1024 * u), 16, vdma_b, key0 * (kD * 2) + 1024 * u, 0, 0);
   };
   // Mask value of key key0 + lane % 32 (one float per lane, lanes l and l + 32 equal).
   auto load_mask = [&](int key0) -> float { return HAS_MASK ? mrow[key0 + c] : 1.0f; };
@@ -475,8 +493,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   };
 
   // Online softmax state (log2 units).  mref: reference max of each of the
-  // lane's two query columns (equal in lanes c and c + 32); initc: -mref
-  // broadcast, the accumulator input of the score MFMAs; l: lane-partial sums.
+  // lane's two query columns (equal in lanes c and c + 32); l: lane-partial sums.
   float mref[2] = {0.0f, 0.0f}, l[2] = {0.0f, 0.0f};
   f32x16 initc[CINIT ? 2 : 1];
 #pragma unroll
@@ -491,21 +508,18 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[dt][nt][e] = 0.0f;
 
-  // S(j) = K Q^T - mref for 32 keys x 64 queries (log2 units).
-  auto scores = [&](const bf16x8 (&kc)[4], f32x16 (&sc)[2]) {
+  // S(j) for query half nt: 32 keys x 32 queries.
+  auto score_half = [&](const bf16x8 (&kc)[4], int nt) -> f32x16 {
+    f32x16 acc;
+    if (CINIT) {
+      acc = initc[CINIT ? nt : 0];
+    } else {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x16 acc;
-      if (CINIT) {
-        acc = initc[nt];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[kk], qf[nt][kk], acc, 0, 0, 0);
-      sc[nt] = acc;
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[kk], qf[nt][kk], acc, 0, 0, 0);
+    return acc;
   };
   // Padding bias for the step whose lane value is mval: nothing when every key
   // is valid, one scalar when all 32 keys share a mask value, per key otherwise.
@@ -531,6 +545,29 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) sc[nt] += bias;
   };
+  // p = 2^(s - mref) for query half nt, rounded to bf16 for the PV product; the
+  // row sums add the rounded values (the ones the product uses).
+  auto softmax_half = [&](f32x16 &sc, int nt, bf16x8 (&pfo)[2]) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const float nm = CINIT ? 0.0f : mref[nt];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      sc[e] = __builtin_amdgcn_exp2f(CINIT ? sc[e] : __builtin_fmaf(sc[e], kLog2e, -nm));
+    float part[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 lo = {sc[8 * s + 0], sc[8 * s + 1], sc[8 * s + 2], sc[8 * s + 3]};
+      const f32x4 hi = {sc[8 * s + 4], sc[8 * s + 5], sc[8 * s + 6], sc[8 * s + 7]};
+      pfo[s] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4),
+                                       0, 1, 2, 3, 4, 5, 6, 7);
+      float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 0, 1), ones, 0.0f, false);
+      float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 2, 3), ones, 0.0f, false);
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 4, 5), ones, a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 6, 7), ones, a1, false);
+      part[s] = a0 + a1;
+    }
+    l[nt] += part[0] + part[1];
+  };
 
   // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
   // bias is added at the top of the iteration that takes its softmax.
@@ -540,19 +577,21 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   float mk_next = load_mask(ck.key0);         // mask of step j + 1
   dma_k(ck.key0, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  f32x16 sA[2], sB[2];
+  f32x16 sc[2];
   {
     bf16x8 kc[4];
     read_k(0, kc);
-    scores(kc, sA);
+    sc[0] = score_half(kc, 0);
+    sc[1] = score_half(kc, 1);
   }
 
   bf16x8 pf[2][2];    // P of the previous step: [nt][key step s]
   bool resc_pending = false;
   float alpha_pending[2] = {1.0f, 1.0f};
-  // One pipeline iteration j: softmax of step j (in s_cur), S(j+1) into
-  // s_next, PV of step j-1.
-  auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+  // One pipeline iteration j: the PV product of step j-1, the softmax of step
+  // j (in sc) and S(j+1), computed half by half into the registers the
+  // softmax of that half has just consumed.
+  auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t) {
     constexpr bool HAS_S = decltype(has_s_t)::value;
     constexpr bool HAS_PV = decltype(has_pv_t)::value;
     constexpr bool FIRST = decltype(first_t)::value;
@@ -560,7 +599,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     bf16x8 kc[4], vt[2][2];
     if (HAS_S) read_k((j + 1) & 1, kc);
     if (HAS_PV) read_vt((j - 1) & 1, vt);
-    apply_mask(s_cur, mk_cur);
+    apply_mask(sc, mk_cur);
     float mk_n2 = 1.0f;
     if (j + 2 < n) {
       ck.advance(p, walk);
@@ -582,11 +621,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     }
     // Rescale decision for step j (before its exponentials).
     {
-      // Scores relative to the reference max (log2 units).
       float ml[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        ml[nt] = CINIT ? tree_max16(s_cur[nt]) : tree_max16(s_cur[nt]) * kLog2e - mref[nt];
+        ml[nt] = CINIT ? tree_max16(sc[nt]) : tree_max16(sc[nt]) * kLog2e - mref[nt];
       const bool need = FIRST || ml[0] > kTauLog2 || ml[1] > kTauLog2;
       if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
@@ -595,7 +633,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
           const float sh = (FIRST || mrow > kTauLog2) ? mrow : 0.0f;
           mref[nt] += sh;
           if (CINIT) {
-            s_cur[nt] -= sh;
+            sc[nt] -= sh;
             initc[CINIT ? nt : 0] -= sh;
           }
           alpha_pending[nt] = __builtin_amdgcn_exp2f(-sh);
@@ -606,57 +644,35 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
       }
     }
 
-    if (HAS_S) scores(kc, s_next);
     if (HAS_PV) {
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
           for (int s = 0; s < 2; ++s)
             o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
     }
-    // Softmax of step j: p = 2^(s - mref), rounded to bf16 for the PV product;
-    // the row sums add the rounded values (the ones the product uses).
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float nm = CINIT ? 0.0f : mref[nt];
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        s_cur[nt][e] = __builtin_amdgcn_exp2f(CINIT ? s_cur[nt][e] : __builtin_fmaf(s_cur[nt][e], kLog2e, -nm));
-      float part[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const f32x4 lo = {s_cur[nt][8 * s + 0], s_cur[nt][8 * s + 1], s_cur[nt][8 * s + 2], s_cur[nt][8 * s + 3]};
-        const f32x4 hi = {s_cur[nt][8 * s + 4], s_cur[nt][8 * s + 5], s_cur[nt][8 * s + 6], s_cur[nt][8 * s + 7]};
-        pf[nt][s] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4),
-                                            0, 1, 2, 3, 4, 5, 6, 7);
-        float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 0, 1), ones, 0.0f, false);
-        float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 2, 3), ones, 0.0f, false);
-        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 4, 5), ones, a0, false);
-        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[nt][s], pf[nt][s], 6, 7), ones, a1, false);
-        part[s] = a0 + a1;
-      }
-      l[nt] += part[0] + part[1];
+    softmax_half(sc[0], 0, pf[0]);
+    if (HAS_S) sc[0] = score_half(kc, 0);
+    softmax_half(sc[1], 1, pf[1]);
+    if (HAS_S) sc[1] = score_half(kc, 1);
+    if (HAS_PV) {
+      BBSA_INTERLEAVE(8, 5);
     }
-    if (HAS_S && HAS_PV) BBSA_INTERLEAVE(16, 6);
-    else BBSA_INTERLEAVE(8, 10);
+    if (HAS_S) {
+      BBSA_INTERLEAVE(4, 10);
+      BBSA_INTERLEAVE(4, 2);
+    }
     mk_cur = mk_next;
     mk_next = mk_n2;
   };
 
   using T = std::true_type;
   using F = std::false_type;
-  iteration(0, T{}, F{}, T{}, sA, sB);
-  sA[0] = sB[0];
-  sA[1] = sB[1];
-  for (int j = 1; j < n - 1; ++j) {
-    iteration(j, T{}, T{}, F{}, sA, sB);
-    sA[0] = sB[0];
-    sA[1] = sB[1];
-  }
-  iteration(n - 1, F{}, T{}, F{}, sA, sB);
+  iteration(0, T{}, F{}, T{});
+  for (int j = 1; j < n - 1; ++j) iteration(j, T{}, T{}, F{});
+  iteration(n - 1, F{}, T{}, F{});
   // Drain: PV of the last step.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (resc_pending) {
