@@ -823,10 +823,11 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
 // ---------------------------------------------------------------- split-K merge
 //
 // One 64-thread workgroup per (batch, head, full row, query tile, 4-query
-// slice); 16 threads per query, each owning 4 consecutive d.  First the
-// maximum M of the chunks' reference maxima, then out = sum_c w_c O_c /
-// sum_c w_c l_c with w_c = 2^(m_c - M) (maxima in log2 units).
+// slice); 16 threads per query, each owning 4 consecutive d:
+// out = sum_c w_c O_c / sum_c w_c l_c with w_c = 2^(m_c - M), M the largest
+// reference maximum (log2 units), accumulated in one pass.
 constexpr int kMergeSlices = kQT / 4;
+constexpr int kMergeBatch = 8;   // chunks whose loads are in flight together
 template <typename OutT>
 __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const int wg = (int)__builtin_amdgcn_workgroup_id_x();
@@ -838,18 +839,36 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const float *base = p.ws + (int64_t)idx * p.chunks * kPartialFloats;
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int q = 4 * slice + (tid >> 4), dq = tid & 15;
-  const int nch = p.chunks;
-  float M = kInitMax;
-#pragma unroll 4
-  for (int ch = 0; ch < nch; ++ch) M = __builtin_fmaxf(M, base[(int64_t)ch * kPartialFloats + kQT * kD + q]);
-  float den = 0.0f;
+  // One pass, kMergeBatch chunks at a time: all loads of a batch are issued
+  // before any of them is used; the running (M, den, acc) is rescaled when a
+  // batch raises the maximum.
+  float M = kInitMax, den = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int ch = 0; ch < nch; ++ch) {
-    const float *part = base + (int64_t)ch * kPartialFloats;
-    const float w = __builtin_amdgcn_exp2f(part[kQT * kD + q] - M);
-    den += w * part[kQT * kD + kQT + q];
-    acc += w * *(const f32x4 *)(part + q * kD + 4 * dq);
+  for (int c0 = 0; c0 < p.chunks; c0 += kMergeBatch) {
+    float mc[kMergeBatch], lc[kMergeBatch];
+    f32x4 oc[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int ch = min(c0 + u, p.chunks - 1);   // repeats stay unused
+      const float *part = base + (int64_t)ch * kPartialFloats;
+      mc[u] = part[kQT * kD + q];
+      lc[u] = part[kQT * kD + kQT + q];
+      oc[u] = *(const f32x4 *)(part + q * kD + 4 * dq);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (c0 + u < p.chunks) Mb = __builtin_fmaxf(Mb, mc[u]);
+    const float r = __builtin_amdgcn_exp2f(M - Mb);
+    den *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = (c0 + u < p.chunks) ? __builtin_amdgcn_exp2f(mc[u] - Mb) : 0.0f;
+      den += w * lc[u];
+      acc += w * oc[u];
+    }
+    M = Mb;
   }
   const f32x4 y = acc * (1.0f / den);
   const int qblock = (p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow;
