@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse attn fwd TFLOP/s (useful) + % MFMA/HBM roofline, L=4096 H=12"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (no sparsity)
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 MFMA
 KERNEL_SOURCES = ["block_sparse_long_bbsa_amd/csrc/bbsa_forward.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bbsa_attn_bf16_B4_H12_L4096.json")
 
@@ -64,15 +65,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(workload_name: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source."""
+    on this workload and on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload_name:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -183,7 +184,8 @@ def main():
 
     flops = useful_flops(w.B, w.H, w.nb, w.block, w.d, w.r)
     nbytes = algorithmic_bytes(w.B, w.H, w.L, w.d, w.nb, w.r, elt)
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_mfma = flops / (peak_mfma * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
     if bound == "hbm":
@@ -191,10 +193,10 @@ def main():
         peak, unit = PEAK_HBM_GBS, "GB/s"
     else:
         achieved = flops / (main_ms * 1e-3) / 1e12
-        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+        peak, unit = peak_mfma, "TFLOP/s"
     value = flops / (ms * 1e-3) / 1e12
     log(f"step {ms * 1e3:.2f} us; main kernel {main_ms * 1e3:.2f} us, merge {comb_ms * 1e3:.2f} us; "
-        f"{value:.1f} useful TFLOP/s; MFMA util {flops / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS:.3f}; "
+        f"{value:.1f} useful TFLOP/s; MFMA util {flops / (main_ms * 1e-3) / 1e12 / peak_mfma:.3f}; "
         f"HBM util {nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f}")
 
     cpu = None
@@ -220,10 +222,10 @@ def main():
                    "algorithmic_mb_per_step": round(nbytes / 1e6, 3), "input_sets": n_sets,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": read_traffic(),
-                     "kernel": "bbsa_attn_bf16", "kernel_us": round(main_ms * 1e3, 3),
+                     "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name),
+                     "kernel": "bbsa_attn_bf16" if w.dtype == "bf16" else "bbsa_attn_f32", "kernel_us": round(main_ms * 1e3, 3),
                      "merge_kernel_us": round(comb_ms * 1e3, 3),
-                     "mfma_frac": round(flops / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "mfma_frac": round(flops / (main_ms * 1e-3) / 1e12 / peak_mfma, 4),
                      "hbm_frac": round(nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": cpu,
     }
