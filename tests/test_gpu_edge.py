@@ -1,0 +1,134 @@
+"""Edge cases of the HIP path against the oracle: workgroup-to-XCD grouping
+with idle slots, general (fractional, leading) padding masks, large scores
+that move the softmax reference often, the plan-size limits, a side stream,
+and the library workspace across shape changes and releases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_bbsa_amd import bbsa, workloads
+from gpu_helpers import announce, assert_close, plans, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bbsa.lib()
+
+
+def _compare(inp, block, r, dtype, seed, what):
+    H = inp["q"].shape[1]
+    nb = inp["q"].shape[2] // block
+    cplan, oplan = plans(H, nb, r, seed)
+    got, st = run_gpu(inp, block, r, dtype, cplan)
+    assert st == bbsa.BBSA_OK
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block)
+    assert_close(got, want, dtype, what)
+
+
+@pytest.mark.parametrize("B,H,L,block,dtype", [
+    (3, 3, 1024, 64, "bf16"),    # 9 (batch, head) pairs: one XCD group serves two, seven serve one
+    (1, 11, 896, 64, "bf16"),    # 11 pairs
+    (5, 3, 1280, 128, "bf16"),   # 15 pairs, block 128
+    (3, 3, 1024, 64, "f32"),
+])
+def test_pairs_not_a_multiple_of_eight(B, H, L, block, dtype):
+    announce(f"pairs B{B} H{H} L{L} block{block} {dtype}")
+    inp = workloads.make_case(B, H, L, 64, 21, dtype=dtype, valid=[L - 37 * (i % 3) for i in range(B)])
+    _compare(inp, block, 2, dtype, 21, f"pairs B{B}xH{H}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fractional_mask_values(dtype):
+    announce(f"fractional mask {dtype}")
+    B, H, L = 2, 2, 1536
+    inp = workloads.make_case(B, H, L, 64, 22, dtype=dtype)
+    rng = np.random.Generator(np.random.PCG64(22))
+    m = rng.uniform(0.0, 1.0, size=(B, L)).astype(np.float32)
+    m[:, : L // 2] = 1.0                  # whole tiles at 1, then mixed values
+    m[0, 1000:1040] = 0.25                # one tile with a single shared value
+    inp["mask"] = m
+    _compare(inp, 64, 3, dtype, 22, "fractional mask")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_leading_padding_moves_reference(dtype):
+    # The first key blocks every query visits are padded: the softmax
+    # reference starts near -10000 and must jump when valid keys arrive.
+    announce(f"leading padding {dtype}")
+    B, H, L = 1, 2, 2048
+    inp = workloads.make_case(B, H, L, 64, 23, dtype=dtype)
+    m = np.ones((B, L), dtype=np.float32)
+    m[:, :64] = 0.0                       # block 0 (a global key block) fully padded
+    m[:, 100:130] = 0.0                   # a partial stretch in block 1
+    inp["mask"] = m
+    _compare(inp, 64, 3, dtype, 23, "leading padding")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_scores_rescale_often(dtype):
+    # q not scaled down: scores ~ N(0, 64), the running maximum moves by more
+    # than the lazy-rescale threshold many times per row.
+    announce(f"large scores {dtype}")
+    inp = workloads.make_case(2, 2, 2048, 64, 24, dtype=dtype, valid=(2048, 1900), q_scale=1.0)
+    _compare(inp, 64, 3, dtype, 24, "large scores")
+
+
+@pytest.mark.parametrize("r,L,block", [(1, 1024, 64), (12, 4096, 64), (20, 8192, 128)])
+def test_random_block_counts(r, L, block):
+    announce(f"r={r} L{L} block{block}")
+    inp = workloads.make_case(1, 2, L, 64, 25 + r, valid=(L - 200,))
+    _compare(inp, block, r, "bf16", 25 + r, f"r={r}")
+
+
+def test_plan_limit_is_reported():
+    # 5 + r > 64 key blocks per middle row is outside what a wavefront lists.
+    nb = 140
+    L = nb * 64
+    q = torch.zeros((1, 1, L, 64), dtype=torch.bfloat16, device="cuda")
+    ra = torch.ones((1, nb - 2, 60), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        bbsa.bbsa_forward(q, q, q, None, ra, 64, 60)
+
+
+def test_side_stream_matches_default_stream():
+    announce("side stream")
+    inp = workloads.make_case(2, 3, 2048, 64, 26, valid=(2048, 1777))
+    plan = bbsa.bbsa_plan_rand_attn(3, 32, 3, 26)
+    q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    mask = to_dev(inp["mask"], torch.float32)
+    ra = torch.from_numpy(plan).cuda()
+    ref, _ = bbsa.bbsa_forward(q, k, v, mask, ra, 64, 3)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out, st = bbsa.bbsa_forward(q, k, v, mask, ra, 64, 3)
+    side.synchronize()
+    assert st == bbsa.BBSA_OK
+    assert torch.equal(out, ref)
+
+
+def test_workspace_regrows_and_releases():
+    # Shapes whose split-K workspace grows, shrinks and grows again, with a
+    # release in between; every result must equal a fresh run's.
+    announce("workspace")
+    cases = [(1, 2, 8192, 64), (2, 2, 2048, 64), (1, 3, 16384, 64)]
+    results = []
+    for B, H, L, block in cases:
+        inp = workloads.make_case(B, H, L, 64, 27, valid=(L - 100,) * B)
+        plan = bbsa.bbsa_plan_rand_attn(H, L // block, 3, 27)
+        results.append((inp, plan, block))
+    outs = []
+    for inp, plan, block in results + results:
+        got, st = run_gpu(inp, block, 3, "bf16", plan)
+        assert st == bbsa.BBSA_OK
+        outs.append(got)
+        if len(outs) == 2:
+            bbsa.bbsa_release_workspace()
+    for i in range(len(results)):
+        assert np.array_equal(outs[i], outs[i + len(results)]), f"case {i} changed across workspace reuse"
