@@ -7,7 +7,9 @@ block=64, r=3, bf16, padded sequences, plan precomputed on the host (a layer
 builds its plan once).  Inputs are resident in HBM before timing starts; the
 steps rotate over several copies of the inputs (more bytes than the 256 MB
 last-level cache) so that no step reads its inputs from cache left by the
-previous one.
+previous one.  The JSON line also carries the 10th/50th/90th percentile of
+single steps each bracketed by its own events, and the warm-cache step time
+(the same input set every step) for comparison.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
 """
@@ -172,6 +174,26 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
+    # Per-step distribution: each step bracketed by its own events.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(args.steps, 1000))]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    p10, p50, p90 = (float(np.percentile(per_step, x)) for x in (10, 50, 90))
+
+    # Warm: the same input set every step (inputs can stay in the 256 MB cache).
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for i in range(args.steps):
+        step(0)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e2.elapsed_time(e3) / args.steps * 1e3
+
     # Same steps again with the library's own HIP events around each kernel.
     bbsa.bbsa_timing_enable(True)
     for i in range(min(args.steps, 4096)):
@@ -195,7 +217,8 @@ def main():
         achieved = flops / (main_ms * 1e-3) / 1e12
         peak, unit = peak_mfma, "TFLOP/s"
     value = flops / (ms * 1e-3) / 1e12
-    log(f"step {ms * 1e3:.2f} us; main kernel {main_ms * 1e3:.2f} us, merge {comb_ms * 1e3:.2f} us; "
+    log(f"step {ms * 1e3:.2f} us (p10/p50/p90 of single steps {p10:.1f}/{p50:.1f}/{p90:.1f}, warm {warm_us:.1f}); "
+        f"main kernel {main_ms * 1e3:.2f} us, merge {comb_ms * 1e3:.2f} us; "
         f"{value:.1f} useful TFLOP/s; MFMA util {flops / (main_ms * 1e-3) / 1e12 / peak_mfma:.3f}; "
         f"HBM util {nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f}")
 
@@ -220,6 +243,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "block": w.block,
                    "r": w.r, "useful_gflop_per_step": round(flops / 1e9, 3),
                    "algorithmic_mb_per_step": round(nbytes / 1e6, 3), "input_sets": n_sets,
+                   "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+                   "warm_step_us": round(warm_us, 2),
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name),
