@@ -770,34 +770,59 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  WalkCursor cur;
-  cur.start(p, walk);
-  for (int step = 0; step < walk.n_steps; ++step) {
-    if (step > 0) cur.advance(p, walk);
-    const int key0 = cur.key0;
-    f32x4 s[2][4];
+  // Operands of one step: K rows 16mt + c (d = 16g .. 16g+15) and the V
+  // values of keys 16mt + 4g + i at d = c + 16dt.  The next step's are loaded
+  // while the current one is computed.
+  struct StepOperands {
+    float kf[2][16];
+    float va[2][4][4];
+    f32x4 mc[2];
+  };
+  auto load_step = [&](int key0, StepOperands &x) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      float kf[16];
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const f32x4 x = *(const f32x4 *)(K + (int64_t)(key0 + 16 * mt + c) * kD + 16 * g + 4 * s4);
+        const f32x4 v4 = *(const f32x4 *)(K + (int64_t)(key0 + 16 * mt + c) * kD + 16 * g + 4 * s4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kf[4 * s4 + e] = x[e];
+        for (int e = 0; e < 4; ++e) x.kf[mt][4 * s4 + e] = v4[e];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float *vrow = V + (int64_t)(key0 + 16 * mt + 4 * g + i) * kD + c;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) x.va[mt][i][dt] = vrow[16 * dt];
+      }
+    }
+    if (HAS_MASK) {
+      x.mc[0] = *(const f32x4 *)(mrow + key0 + 4 * g);
+      x.mc[1] = *(const f32x4 *)(mrow + key0 + 16 + 4 * g);
+    }
+  };
+
+  WalkCursor cur;
+  cur.start(p, walk);
+  StepOperands nxt;
+  load_step(cur.key0, nxt);
+  for (int step = 0; step < walk.n_steps; ++step) {
+    const StepOperands x = nxt;
+    if (step + 1 < walk.n_steps) {
+      cur.advance(p, walk);
+      load_step(cur.key0, nxt);
+    }
+    f32x4 s[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[ks], qf[nt][ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.kf[mt][ks], qf[nt][ks], acc, 0, 0, 0);
         s[mt][nt] = acc;
       }
-    }
     if (HAS_MASK) {
-      f32x4 mc[2];
-      mc[0] = *(const f32x4 *)(mrow + key0 + 4 * g);
-      mc[1] = *(const f32x4 *)(mrow + key0 + 16 + 4 * g);
+      f32x4 mc[2] = {x.mc[0], x.mc[1]};
       apply_mask(s, mc);
     }
     softmax_rescale(s, st, o);
@@ -806,16 +831,12 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float *vrow = V + (int64_t)(key0 + 16 * mt + 4 * g + i) * kD + c;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const float va = vrow[16 * dt];
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt)
-            o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, s[mt][nt][i], o[dt][nt], 0, 0, 0);
-        }
-      }
+            o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.va[mt][i][dt], s[mt][nt][i], o[dt][nt], 0, 0, 0);
   }
   finish_item<float>(p, it, q0, st, o);
 }
@@ -946,8 +967,9 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   p.B = B; p.H = H; p.L = L; p.nb = nb; p.block = block; p.r = r;
   p.qtiles = block / kQT;
   p.n_rows_global = full ? nb : 2;
-  // Full rows are cut into chunks of 1024 keys so they do not form the tail.
-  p.chunk_blocks = 1024 / block;
+  // Full rows are cut into chunks (1024 keys for bf16, 256 for the slower
+  // fp32 path) so they do not form the tail.
+  p.chunk_blocks = (dtype == BBSA_F32 ? 256 : 1024) / block;
   if (p.chunk_blocks > nb) p.chunk_blocks = nb;
   p.chunks = (nb + p.chunk_blocks - 1) / p.chunk_blocks;
   p.n_global_items = p.n_rows_global * p.qtiles * p.chunks;
