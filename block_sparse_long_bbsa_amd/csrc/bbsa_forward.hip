@@ -240,7 +240,7 @@ struct WalkCursor {
   __device__ inline void start(const Params &p, const KeyWalk &w) {
     t = 0;
     sb = 0;
-    key0 = w.first_blk * p.block;   // uniform: does not wait for the plan load
+    key0 = __builtin_amdgcn_readfirstlane(w.first_blk * p.block);   // uniform; no plan entry needed
   }
   __device__ inline void advance(const Params &p, const KeyWalk &w) {
     if (++sb == w.steps_per_block) {
@@ -253,7 +253,12 @@ struct WalkCursor {
   }
 };
 
-__device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
+// The key block list of an item, in two parts so that the plan entries can
+// be loaded early and used late: make_walk_base fills everything but the
+// random blocks and starts the load of the lane's plan entry (rnd; rslot is
+// the lane's slot in the plan row, -1 if none); merge_plan puts the random
+// blocks in (clamped so that a bad plan never reads outside the sequence).
+__device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int &rnd, int &rslot) {
   const int lane = (int)__builtin_amdgcn_workitem_id_x();
   KeyWalk w;
   w.steps_per_block = p.block / kStep;
@@ -266,20 +271,33 @@ __device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
   w.n_steps = __builtin_amdgcn_readfirstlane(nblk * w.steps_per_block);
   w.first_blk = middle ? 0 : first;
   int blk;
+  rslot = -1;
+  rnd = 0;
   if (middle) {
     // Middle query block i: the two global blocks, the window without them,
-    // then the random blocks (clamped so a bad plan never reads outside).
+    // then the random blocks.
     const int w0 = (i == 1) ? 1 : i - 1;
     const int h = it.bh % p.H;
     const int32_t *ra_row = p.rand_attn + ((int64_t)h * (p.nb - 2) + (i - 1)) * p.r;
+    const int t = lane - 2 - nw;
+    rnd = ra_row[min(max(t, 0), p.r - 1)];
+    rslot = (t >= 0 && t < p.r) ? t : -1;
     blk = 0;
     if (lane == 1) blk = p.nb - 1;
     else if (lane >= 2 && lane < 2 + nw) blk = w0 + (lane - 2);
-    else if (lane >= 2 + nw && lane < 2 + nw + p.r) blk = min(max(ra_row[lane - 2 - nw], 0), p.nb - 1);
   } else {
     blk = first + min(lane, nblk - 1);
   }
   w.blk = blk;
+  return w;
+}
+__device__ inline void merge_plan(const Params &p, KeyWalk &w, int rnd, int rslot) {
+  if (rslot >= 0) w.blk = min(max(rnd, 0), p.nb - 1);
+}
+__device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
+  int rnd, rslot;
+  KeyWalk w = make_walk_base(p, it, rnd, rslot);
+  merge_plan(p, w, rnd, rslot);
   return w;
 }
 
@@ -444,7 +462,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
       }
   }
 
-  const KeyWalk walk = make_walk(p, it);
+  // The plan entries are merged into the walk after the prologue's wait: the
+  // first two K tiles lie in the first block and do not need them.
+  int rnd, rslot;
+  KeyWalk walk = make_walk_base(p, it, rnd, rslot);
   const int n = walk.n_steps;                 // >= 2
   WalkCursor ck, cv;                          // K runs two steps ahead of V
   ck.start(p, walk);
@@ -577,6 +598,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   float mk_next = load_mask(ck.key0);         // mask of step j + 1
   dma_k(ck.key0, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  merge_plan(p, walk, rnd, rslot);
   f32x16 sc[2];
   {
     bf16x8 kc[4];
