@@ -14,9 +14,7 @@
 //   * bf16 path: scores are computed transposed, S^T = K Q^T, on MFMA
 //     32x32x16 bf16, so each lane holds 16 keys of one query column and the
 //     row max needs a single cross-lane swap; a probability costs one FMA
-//     (score * log2(e) - reference max) and one v_exp_f32 (the BBSA_CINIT
-//     build option instead folds both into a log2(e)-scaled Q and the MFMA
-//     accumulator input);
+//     (score * log2(e) - reference max) and one v_exp_f32;
 //   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
 //     XOR-swizzled rows); K is read back as the MFMA A operand, V is read back
 //     transposed with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T;
@@ -395,14 +393,8 @@ __device__ inline float swap_halves(float x) {
   return __uint_as_float(lane < 32 ? a[1] : a[0]);
 }
 
-// CINIT: subtract the reference max through the MFMA accumulator input (costs
-// 32 registers); otherwise one v_sub per score.
-#ifndef BBSA_CINIT
-#define BBSA_CINIT 0
-#endif
 template <bool HAS_MASK>
 __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
-  constexpr bool CINIT = BBSA_CINIT;
   const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x());
   if (it.bh >= p.bh_total) return;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kTileBytes];
@@ -441,25 +433,15 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     }
   }
 
-  // Q^T operand: lane (c, h) holds Q[q0 + 32nt + c][16k + 8h .. +7]; with
-  // CINIT the values are pre-scaled by log2(e) (rounded to bf16) so that the
-  // MFMA accumulates scores in log2 units.
+  // Q^T operand: lane (c, h) holds Q[q0 + 32nt + c][16k + 8h .. +7].
   bf16x8 qf[2][4];
   {
     const bf16_t *Q = (const bf16_t *)p.q + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 raw = *(const bf16x8 *)(Q + (int64_t)(32 * nt + c) * kD + 16 * kk + 8 * h);
-        if (CINIT) {
-          typedef float f32x8 __attribute__((ext_vector_type(8)));
-          const f32x8 f = __builtin_convertvector(raw, f32x8) * kLog2e;
-          qf[nt][kk] = __builtin_convertvector(f, bf16x8);
-        } else {
-          qf[nt][kk] = raw;
-        }
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        qf[nt][kk] = *(const bf16x8 *)(Q + (int64_t)(32 * nt + c) * kD + 16 * kk + 8 * h);
   }
 
   // The plan entries are merged into the walk after the prologue's wait: the
@@ -516,11 +498,6 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   // Online softmax state (log2 units).  mref: reference max of each of the
   // lane's two query columns (equal in lanes c and c + 32); l: lane-partial sums.
   float mref[2] = {0.0f, 0.0f}, l[2] = {0.0f, 0.0f};
-  f32x16 initc[CINIT ? 2 : 1];
-#pragma unroll
-  for (int nt = 0; nt < (CINIT ? 2 : 1); ++nt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) initc[nt][e] = 0.0f;
   f32x16 o[2][2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -532,12 +509,8 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   // S(j) for query half nt: 32 keys x 32 queries.
   auto score_half = [&](const bf16x8 (&kc)[4], int nt) -> f32x16 {
     f32x16 acc;
-    if (CINIT) {
-      acc = initc[CINIT ? nt : 0];
-    } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-    }
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[kk], qf[nt][kk], acc, 0, 0, 0);
     return acc;
@@ -549,7 +522,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     const unsigned long long pad = __builtin_amdgcn_ballot_w64(mval != 1.0f);
     if (!pad) return;
     const float m0 = __builtin_amdgcn_readfirstlane(mval);
-    const float bl = CINIT ? kPadBias * kLog2e : kPadBias;
+    const float bl = kPadBias;
     if (!__builtin_amdgcn_ballot_w64(mval != m0)) {
       const float bias = bl * (1.0f - m0);
 #pragma unroll
@@ -570,10 +543,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   // row sums add the rounded values (the ones the product uses).
   auto softmax_half = [&](f32x16 &sc, int nt, bf16x8 (&pfo)[2]) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const float nm = CINIT ? 0.0f : mref[nt];
+    const float nm = mref[nt];
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      sc[e] = __builtin_amdgcn_exp2f(CINIT ? sc[e] : __builtin_fmaf(sc[e], kLog2e, -nm));
+      sc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], kLog2e, -nm));
     float part[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -646,7 +619,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
       float ml[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        ml[nt] = CINIT ? tree_max16(sc[nt]) : tree_max16(sc[nt]) * kLog2e - mref[nt];
+        ml[nt] = tree_max16(sc[nt]) * kLog2e - mref[nt];
       const bool need = FIRST || ml[0] > kTauLog2 || ml[1] > kTauLog2;
       if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
@@ -654,10 +627,6 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
           const float mrow = __builtin_fmaxf(ml[nt], swap_halves(ml[nt]));
           const float sh = (FIRST || mrow > kTauLog2) ? mrow : 0.0f;
           mref[nt] += sh;
-          if (CINIT) {
-            sc[nt] -= sh;
-            initc[CINIT ? nt : 0] -= sh;
-          }
           alpha_pending[nt] = __builtin_amdgcn_exp2f(-sh);
           if (!FIRST) l[nt] *= alpha_pending[nt];
         }
