@@ -496,8 +496,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   };
 
   // Online softmax state (log2 units).  mref: reference max of each of the
-  // lane's two query columns (equal in lanes c and c + 32); l: lane-partial sums.
-  float mref[2] = {0.0f, 0.0f}, l[2] = {0.0f, 0.0f};
+  // lane's two query columns (equal in lanes c and c + 32); l: lane-partial
+  // row sums, two running chains per column that the dot2 instructions
+  // accumulate into directly (no per-step temporaries).
+  float mref[2] = {0.0f, 0.0f}, l[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
   f32x16 o[2][2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -547,20 +549,17 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       sc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], kLog2e, -nm));
-    float part[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const f32x4 lo = {sc[8 * s + 0], sc[8 * s + 1], sc[8 * s + 2], sc[8 * s + 3]};
       const f32x4 hi = {sc[8 * s + 4], sc[8 * s + 5], sc[8 * s + 6], sc[8 * s + 7]};
       pfo[s] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4),
                                        0, 1, 2, 3, 4, 5, 6, 7);
-      float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 0, 1), ones, 0.0f, false);
-      float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 2, 3), ones, 0.0f, false);
-      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 4, 5), ones, a0, false);
-      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 6, 7), ones, a1, false);
-      part[s] = a0 + a1;
+      l[nt][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 0, 1), ones, l[nt][0], false);
+      l[nt][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 2, 3), ones, l[nt][1], false);
+      l[nt][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 4, 5), ones, l[nt][0], false);
+      l[nt][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pfo[s], pfo[s], 6, 7), ones, l[nt][1], false);
     }
-    l[nt] += part[0] + part[1];
   };
 
   // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
@@ -628,7 +627,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
           const float sh = (FIRST || mrow > kTauLog2) ? mrow : 0.0f;
           mref[nt] += sh;
           alpha_pending[nt] = __builtin_amdgcn_exp2f(-sh);
-          if (!FIRST) l[nt] *= alpha_pending[nt];
+          if (!FIRST) {
+            l[nt][0] *= alpha_pending[nt];
+            l[nt][1] *= alpha_pending[nt];
+          }
         }
         // The first step has no O to rescale.
         resc_pending = !FIRST;
@@ -687,7 +689,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   // Finish: full row sums, then normalised bf16 output or a split-K partial.
   float lsum[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) lsum[nt] = l[nt] + swap_halves(l[nt]);
+  for (int nt = 0; nt < 2; ++nt) {
+    const float lp = l[nt][0] + l[nt][1];
+    lsum[nt] = lp + swap_halves(lp);
+  }
   if (it.grow >= 0 && p.chunks > 1) {
     const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.chunks + it.chunk;
     float *part = p.ws + pidx * kPartialFloats;
