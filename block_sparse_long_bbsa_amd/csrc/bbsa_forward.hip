@@ -449,9 +449,12 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   int rnd, rslot;
   KeyWalk walk = make_walk_base(p, it, rnd, rslot);
   const int n = walk.n_steps;                 // >= 2
-  WalkCursor ck, cv;                          // K runs two steps ahead of V
-  ck.start(p, walk);
-  cv.start(p, walk);
+  // First key of step i: block i / steps_per_block of the list (a lane of
+  // walk.blk), then 32 keys per step inside it.  Branch-free; uniform.
+  const int lg_spb = walk.steps_per_block >> 1;      // steps_per_block is 2 or 4
+  auto key_of = [&](int i) -> int {
+    return __builtin_amdgcn_readlane(walk.blk, i >> lg_spb) * p.block + (i & (walk.steps_per_block - 1)) * kStep;
+  };
 
   // K and V of this (batch, head) as buffer resources: the DMA source of a
   // lane is a 32-bit per-lane offset plus a scalar offset for the step, and
@@ -460,21 +463,27 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
       __builtin_amdgcn_make_buffer_rsrc((void *)Kbh, (short)0, p.L * kD * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void *)Vbh, (short)0, p.L * kD * 2, kBufferWord3);
+  // The instruction offset 1024u moves both the LDS destination and the
+  // source by 1024u bytes: one M0 value per tile.
   int kdma_b[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) kdma_b[u] = 2 * kdma[u];
+  for (int u = 0; u < 4; ++u) kdma_b[u] = 2 * kdma[u] - 1024 * u;
   const int vdma_b = 2 * vdma;
   auto dma_k = [&](int key0, int slot) {
     unsigned char *dst = kbuf + slot * kTileBytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)(dst + 1024 * u), 16, kdma_b[u], key0 * (kD * 2), 0, 0);
+    const int so = key0 * (kD * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[3], so, 3072, 0);
   };
   auto dma_v = [&](int key0, int slot) {
     unsigned char *dst = vbuf + slot * kTileBytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)(dst + 1024 * u), 16, vdma_b, key0 * (kD * 2) + 1024 * u, 0, 0);
+    const int so = key0 * (kD * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 3072, 0);
   };
   // Mask value of key key0 + lane % 32 (one float per lane, lanes l and l + 32 equal).
   auto load_mask = [&](int key0) -> float { return HAS_MASK ? mrow[key0 + c] : 1.0f; };
@@ -564,11 +573,11 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 
   // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
   // bias is added at the top of the iteration that takes its softmax.
-  float mk_cur = load_mask(ck.key0);          // mask of step j (j = 0)
-  dma_k(ck.key0, 0);
-  ck.advance(p, walk);
-  float mk_next = load_mask(ck.key0);         // mask of step j + 1
-  dma_k(ck.key0, 1);
+  const int key_0 = key_of(0), key_1 = key_of(1);
+  float mk_cur = load_mask(key_0);            // mask of step j (j = 0)
+  dma_k(key_0, 0);
+  float mk_next = load_mask(key_1);           // mask of step j + 1
+  dma_k(key_1, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   merge_plan(p, walk, rnd, rslot);
   f32x16 sc[2];
@@ -585,23 +594,23 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   // One pipeline iteration j: the PV product of step j-1, the softmax of step
   // j (in sc) and S(j+1), computed half by half into the registers the
   // softmax of that half has just consumed.
-  auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t) {
+  auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t, auto steady_t) {
     constexpr bool HAS_S = decltype(has_s_t)::value;
     constexpr bool HAS_PV = decltype(has_pv_t)::value;
     constexpr bool FIRST = decltype(first_t)::value;
+    constexpr bool STEADY = decltype(steady_t)::value;   // j + 2 < n
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K(j+1), V(j-1), mask(j+2) from iteration j-1
     bf16x8 kc[4], vt[2][2];
     if (HAS_S) read_k((j + 1) & 1, kc);
     if (HAS_PV) read_vt((j - 1) & 1, vt);
     apply_mask(sc, mk_cur);
     float mk_n2 = 1.0f;
-    if (j + 2 < n) {
-      ck.advance(p, walk);
-      mk_n2 = load_mask(ck.key0);
-      dma_k(ck.key0, j & 1);
+    if (STEADY || j + 2 < n) {
+      const int kk0 = key_of(j + 2);
+      mk_n2 = load_mask(kk0);
+      dma_k(kk0, j & 1);
     }
-    dma_v(cv.key0, j & 1);
-    cv.advance(p, walk);
+    dma_v(key_of(j), j & 1);
 
     // A rescale decided in the previous iteration applies to O now: after the
     // PV product of step j-2 and before that of step j-1 (whose probabilities
@@ -663,9 +672,11 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 
   using T = std::true_type;
   using F = std::false_type;
-  iteration(0, T{}, F{}, T{});
-  for (int j = 1; j < n - 1; ++j) iteration(j, T{}, T{}, F{});
-  iteration(n - 1, F{}, T{}, F{});
+  iteration(0, T{}, F{}, T{}, F{});
+  int j = 1;
+  for (; j + 2 < n; ++j) iteration(j, T{}, T{}, F{}, T{});
+  for (; j < n - 1; ++j) iteration(j, T{}, T{}, F{}, F{});
+  iteration(n - 1, F{}, T{}, F{}, F{});
   // Drain: PV of the last step.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (resc_pending) {
