@@ -64,6 +64,26 @@ constexpr float kInitMax = -1.0e30f;
 // units), then the 64 row sums.
 constexpr int kPartialFloats = kQT * kD + 2 * kQT;
 
+// Division of 31-bit non-negative integers by a divisor fixed at launch:
+// q = (mulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1 (the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.s = 0;
+  while ((1ull << f.s) < d) ++f.s;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
+  return f;
+}
+__device__ inline int fdiv(int n, const FastDiv &f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)n * f.m) >> 32);
+  return (int)((hi + (uint32_t)n) >> f.s);
+}
+
 struct Params {
   const void *q, *k, *v;
   const float *mask;         // [B, L] or null
@@ -80,6 +100,13 @@ struct Params {
   int items_per_bh;          // n_global_items + middle items
   int bh_total;              // B * H
   int xcd_remap;             // 1: map workgroups so one (batch, head) stays on one XCD
+  int n_glob;                // full-row items before the first middle item (per XCD lane)
+  FastDiv div_global;        // n_global_items
+  FastDiv div_mid;           // middle items per (batch, head), at least 1
+  FastDiv div_row;           // qtiles * chunks
+  FastDiv div_chunks;        // chunks
+  FastDiv div_qtiles;        // qtiles
+  FastDiv div_heads;         // H
 };
 
 // A work item: 64 query rows (query tile qt of query block qblock) of one
@@ -99,29 +126,29 @@ struct Item {
 // With the XCD remap, workgroup w runs on XCD x = w % 8 and serves only the
 // (batch, head) pairs x, x + 8, x + 16, ..., so all items of one pair share
 // one L2.
+// All divisions use the launch's precomputed FastDiv constants.
 __device__ inline Item decode_item(const Params &p, int wg) {
-  const int lanes = p.xcd_remap ? 8 : 1;
-  const int x = p.xcd_remap ? (wg & 7) : 0, slot = p.xcd_remap ? (wg >> 3) : wg;
-  const int per_x = (p.bh_total + lanes - 1) / lanes;     // pairs served per XCD
-  const int n_glob = per_x * p.n_global_items;
-  const int n_mid = max(p.items_per_bh - p.n_global_items, 1);
-  const bool g = slot < n_glob;
-  const int s2 = slot - n_glob;
-  const int j = g ? slot / p.n_global_items : s2 / n_mid;
-  const int local = g ? slot % p.n_global_items : p.n_global_items + s2 % n_mid;
-  const int bh = x + lanes * j;
+  const int lg_lanes = p.xcd_remap ? 3 : 0;
+  const int x = wg & ((1 << lg_lanes) - 1), slot = wg >> lg_lanes;
+  const bool g = slot < p.n_glob;
+  const int sg = g ? slot : 0, sm = g ? 0 : slot - p.n_glob;
+  const int jg = fdiv(sg, p.div_global), jm = fdiv(sm, p.div_mid);
+  const int j = g ? jg : jm;
+  const int local = g ? sg - jg * p.n_global_items : p.n_global_items + (sm - jm * (int)p.div_mid.d);
+  const int bh = x + (j << lg_lanes);
   const bool global_row = local < p.n_global_items;
-  const int per_row = p.qtiles * p.chunks;
-  const int m = local - p.n_global_items;
-  const int grow = global_row ? local / per_row : -1;
-  const int rem = global_row ? local % per_row : 0;
+  const int lr = global_row ? local : 0;
+  const int m = global_row ? 0 : local - p.n_global_items;
+  const int grow = fdiv(lr, p.div_row);
+  const int rem = lr - grow * (int)p.div_row.d;
+  const int qt_g = fdiv(rem, p.div_chunks);
+  const int mq = fdiv(m, p.div_qtiles);
   Item it;
   it.bh = bh;   // >= bh_total marks an idle workgroup
-  it.grow = grow;
-  it.qt = global_row ? rem / p.chunks : m % p.qtiles;
-  it.chunk = global_row ? rem % p.chunks : 0;
-  it.qblock = global_row ? ((p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow)
-                         : 1 + m / p.qtiles;
+  it.grow = global_row ? grow : -1;
+  it.qt = global_row ? qt_g : m - mq * p.qtiles;
+  it.chunk = global_row ? rem - qt_g * p.chunks : 0;
+  it.qblock = global_row ? ((p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow) : 1 + mq;
   return it;
 }
 
@@ -275,7 +302,7 @@ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int &r
     // Middle query block i: the two global blocks, the window without them,
     // then the random blocks.
     const int w0 = (i == 1) ? 1 : i - 1;
-    const int h = it.bh % p.H;
+    const int h = it.bh - fdiv(it.bh, p.div_heads) * p.H;
     const int32_t *ra_row = p.rand_attn + ((int64_t)h * (p.nb - 2) + (i - 1)) * p.r;
     const int t = lane - 2 - nw;
     rnd = ra_row[min(max(t, 0), p.r - 1)];
@@ -404,7 +431,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   const int lane = (int)__builtin_amdgcn_workitem_id_x();
   const int c = lane & 31, h = lane >> 5;             // MFMA 32x32 lane coordinates
   const int G = lane >> 4, cc = lane & 15;            // 16-lane groups of the transposed reads
-  const int b = it.bh / p.H;
+  const int b = fdiv(it.bh, p.div_heads);
   const bf16_t *Kbh = (const bf16_t *)p.k + (int64_t)it.bh * p.seq_stride;
   const bf16_t *Vbh = (const bf16_t *)p.v + (int64_t)it.bh * p.seq_stride;
   const float *mrow = HAS_MASK ? p.mask + (int64_t)b * p.L : nullptr;
@@ -750,7 +777,7 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
   const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x());
   if (it.bh >= p.bh_total) return;
   const int lane = (int)__builtin_amdgcn_workitem_id_x(), c = lane & 15, g = lane >> 4;
-  const int b = it.bh / p.H;
+  const int b = fdiv(it.bh, p.div_heads);
   const float *Q = (const float *)p.q + (int64_t)it.bh * p.seq_stride;
   const float *K = (const float *)p.k + (int64_t)it.bh * p.seq_stride;
   const float *V = (const float *)p.v + (int64_t)it.bh * p.seq_stride;
@@ -991,6 +1018,13 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
     return BBSA_ERR_UNSUPPORTED;
   p.items_per_bh = (int)items_per_bh;
   p.bh_total = (int)bh;
+  p.n_glob = (int)((p.xcd_remap ? (bh + 7) / 8 : bh) * p.n_global_items);
+  p.div_global = make_fastdiv((uint32_t)p.n_global_items);
+  p.div_mid = make_fastdiv((uint32_t)std::max(n_middle, 1));
+  p.div_row = make_fastdiv((uint32_t)(p.qtiles * p.chunks));
+  p.div_chunks = make_fastdiv((uint32_t)p.chunks);
+  p.div_qtiles = make_fastdiv((uint32_t)p.qtiles);
+  p.div_heads = make_fastdiv((uint32_t)H);
   if (n_partials > 0) {
     const int rc = ensure_workspace((size_t)n_partials * kPartialFloats * sizeof(float), &p.ws);
     if (rc != BBSA_OK) return rc;
