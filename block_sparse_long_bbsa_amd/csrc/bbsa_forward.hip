@@ -734,6 +734,9 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
   if (it.grow >= 0 && p.chunks > 1) {
     const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.chunks + it.chunk;
     float *part = p.ws + pidx * kPartialFloats;
+    // The 64 x 64 fp32 tile is staged in LDS (all four K/V buffers) so that
+    // the stores are whole 256-byte rows: 16-byte chunk k of row q sits at
+    // chunk k ^ (q & 15) of the LDS row.
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -741,8 +744,18 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const f32x4 y = {o[dt][nt][4 * jj], o[dt][nt][4 * jj + 1], o[dt][nt][4 * jj + 2], o[dt][nt][4 * jj + 3]};
-          *(f32x4 *)(part + (32 * nt + c) * kD + 32 * dt + 8 * jj + 4 * h) = y;
+          const int q = 32 * nt + c, k = 8 * dt + 2 * jj + h;
+          *(f32x4 *)(lds + q * 256 + 16 * (k ^ (q & 15))) = y;
         }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS (one wavefront per workgroup)
+    {
+      const int k = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = 4 * i + (lane >> 4);
+        *(f32x4 *)(part + q * kD + 4 * k) = *(const f32x4 *)(lds + q * 256 + 16 * (k ^ (q & 15)));
+      }
+    }
     if (h == 0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -752,18 +765,34 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     }
     return;
   }
-  bf16_t *out = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
+  // The normalised 64 x 64 bf16 tile goes through LDS (the free K buffers)
+  // so that the global stores are whole 128-byte rows: 16-byte chunk k of
+  // row q sits at chunk k ^ (q & 7) of the LDS row.
+  {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float inv = 1.0f / lsum[nt];
-    bf16_t *row = out + (int64_t)(32 * nt + c) * kD;
+    for (int nt = 0; nt < 2; ++nt) {
+      const float inv = 1.0f / lsum[nt];
+      const int q = 32 * nt + c;
+      unsigned char *lrow = kbuf + q * 128;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 y = {o[dt][nt][4 * jj], o[dt][nt][4 * jj + 1], o[dt][nt][4 * jj + 2], o[dt][nt][4 * jj + 3]};
-        *(bf16x4 *)(row + 32 * dt + 8 * jj + 4 * h) = __builtin_convertvector(y * inv, bf16x4);
-      }
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 y = {o[dt][nt][4 * jj], o[dt][nt][4 * jj + 1], o[dt][nt][4 * jj + 2], o[dt][nt][4 * jj + 3]};
+          *(bf16x4 *)(lrow + 16 * ((4 * dt + jj) ^ (q & 7)) + 8 * h) = __builtin_convertvector(y * inv, bf16x4);
+        }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS (one wavefront per workgroup)
+  {
+    bf16_t *out = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
+    const int ch = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = 8 * i + (lane >> 3);
+      const bf16x8 v = *(const bf16x8 *)(kbuf + q * 128 + 16 * (ch ^ (q & 7)));
+      *(bf16x8 *)(out + (int64_t)q * kD + 8 * ch) = v;
+    }
   }
 }
 
