@@ -791,7 +791,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     for (int i = 0; i < 8; ++i) {
       const int q = 8 * i + (lane >> 3);
       const bf16x8 v = *(const bf16x8 *)(kbuf + q * 128 + 16 * (ch ^ (q & 7)));
-      *(bf16x8 *)(out + (int64_t)q * kD + 8 * ch) = v;
+      __builtin_nontemporal_store(v, (bf16x8 *)(out + (int64_t)q * kD + 8 * ch));   // never re-read here
     }
   }
 }
