@@ -94,8 +94,9 @@ struct Params {
   int B, H, L, nb, block, r;
   int qtiles;                // block / 64
   int n_rows_global;         // query blocks handled as full rows: 2, or nb on the fallback
-  int chunks;                // key chunks per full row
-  int chunk_blocks;          // key blocks per chunk
+  int chunks;                // key chunks per full row (block range [c nb / chunks, (c + 1) nb / chunks))
+  int group;                 // items per workgroup: 4 on the bf16 path (a full row's chunks in fours), else 1
+  int nparts;                // split-K partials per full row left for the merge kernel: chunks / group
   int n_global_items;        // per (batch, head): n_rows_global * qtiles * chunks
   int items_per_bh;          // n_global_items + middle items
   int bh_total;              // B * H
@@ -126,10 +127,14 @@ struct Item {
 // With the XCD remap, workgroup w runs on XCD x = w % 8 and serves only the
 // (batch, head) pairs x, x + 8, x + 16, ..., so all items of one pair share
 // one L2.
+// With p.group items per workgroup, wavefront wv of workgroup wg takes item
+// wv of the workgroup's run of p.group consecutive items; the full-row items
+// of a pair come as whole groups (their count is a multiple of p.group), so
+// a group of full-row items is the p.group chunks of one row tile.
 // All divisions use the launch's precomputed FastDiv constants.
-__device__ inline Item decode_item(const Params &p, int wg) {
+__device__ inline Item decode_item(const Params &p, int wg, int wv) {
   const int lg_lanes = p.xcd_remap ? 3 : 0;
-  const int x = wg & ((1 << lg_lanes) - 1), slot = wg >> lg_lanes;
+  const int x = wg & ((1 << lg_lanes) - 1), slot = (wg >> lg_lanes) * p.group + wv;
   const bool g = slot < p.n_glob;
   const int sg = g ? slot : 0, sm = g ? 0 : slot - p.n_glob;
   const int jg = fdiv(sg, p.div_global), jm = fdiv(sm, p.div_mid);
@@ -283,16 +288,18 @@ struct WalkCursor {
 // random blocks and starts the load of the lane's plan entry (rnd; rslot is
 // the lane's slot in the plan row, -1 if none); merge_plan puts the random
 // blocks in (clamped so that a bad plan never reads outside the sequence).
+__device__ inline int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() & 63; }
+
 __device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int &rnd, int &rslot) {
-  const int lane = (int)__builtin_amdgcn_workitem_id_x();
+  const int lane = lane_id();
   KeyWalk w;
   w.steps_per_block = p.block / kStep;
   // Uniform quantities first (kept in scalar registers), then the per-lane list.
   const bool middle = it.grow < 0;
   const int i = it.qblock;
   const int nw = (i == 1 || i == p.nb - 2) ? 2 : 3;
-  const int first = it.chunk * p.chunk_blocks;
-  const int nblk = middle ? 2 + nw + p.r : min(p.chunk_blocks, p.nb - first);
+  const int first = fdiv(it.chunk * p.nb, p.div_chunks);
+  const int nblk = middle ? 2 + nw + p.r : fdiv((it.chunk + 1) * p.nb, p.div_chunks) - first;   // may be 0 if nb < chunks
   w.n_steps = __builtin_amdgcn_readfirstlane(nblk * w.steps_per_block);
   w.first_blk = middle ? 0 : first;
   int blk;
@@ -311,7 +318,7 @@ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int &r
     if (lane == 1) blk = p.nb - 1;
     else if (lane >= 2 && lane < 2 + nw) blk = w0 + (lane - 2);
   } else {
-    blk = first + min(lane, nblk - 1);
+    blk = first + max(min(lane, nblk - 1), 0);
   }
   w.blk = blk;
   return w;
@@ -335,8 +342,8 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, Soft
   float lsum[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) lsum[nt] = group4_sum(st.l[nt]);
-  if (it.grow >= 0 && p.chunks > 1) {
-    const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.chunks + it.chunk;
+  if (it.grow >= 0 && p.nparts > 1) {
+    const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.nparts + it.chunk;
     float *part = p.ws + pidx * kPartialFloats;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -416,19 +423,34 @@ __device__ inline float tree_max16(const f32x16 &v) {
 // Value of the other half of the wavefront (lane l ^ 32).
 __device__ inline float swap_halves(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const int lane = (int)__builtin_amdgcn_workitem_id_x();
+  const int lane = lane_id();
   return __uint_as_float(lane < 32 ? a[1] : a[0]);
 }
 
+constexpr int kGroup = 4;                        // wavefronts (items) per bf16 workgroup
+constexpr int kWaveLds = 4 * kTileBytes;          // 16 KB per wavefront: K and V double buffers
+
+// One wavefront per item, kGroup items per workgroup.  The wavefronts of a
+// workgroup run independent items, except that a group of full-row items is
+// the kGroup key chunks of one row tile: those merge their partial results
+// through LDS at the end (one barrier), so a row of up to kGroup chunks
+// needs no separate merge kernel.
 template <bool HAS_MASK>
-__global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
-  const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x());
+__global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
+  const int wv = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_workitem_id_x() >> 6);
+  const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x(), wv);
+  // Idle items only occur as whole groups of full-row items or among middle
+  // rows, so no wavefront that leaves here is awaited at the merge barrier.
   if (it.bh >= p.bh_total) return;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kTileBytes];
+  // kGroup wavefront regions first (the LDS transfers address the first
+  // 64 KB), then the full-row merge's per-row maxima and sums.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_all[kGroup * kWaveLds + kGroup * 2 * kQT * 4];
+  unsigned char *const lds = lds_all + wv * kWaveLds;
   unsigned char *const kbuf = lds;                    // K tile i at kbuf + (i & 1) * kTileBytes
   unsigned char *const vbuf = lds + 2 * kTileBytes;   // V tiles
+  float *const merge_ml = (float *)(lds_all + kGroup * kWaveLds);   // [wavefront][64 maxima, 64 sums]
 
-  const int lane = (int)__builtin_amdgcn_workitem_id_x();
+  const int lane = lane_id();
   const int c = lane & 31, h = lane >> 5;             // MFMA 32x32 lane coordinates
   const int G = lane >> 4, cc = lane & 15;            // 16-lane groups of the transposed reads
   const int b = fdiv(it.bh, p.div_heads);
@@ -598,6 +620,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     }
   };
 
+  if (n == 0) {
+    // An empty key chunk (a row shorter than kGroup blocks): a neutral partial.
+    mref[0] = mref[1] = kInitMax;
+  } else {
   // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
   // bias is added at the top of the iteration that takes its softmax.
   const int key_0 = key_of(0), key_1 = key_of(1);
@@ -723,6 +749,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
         for (int s = 0; s < 2; ++s)
           o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
   }
+  }   // n > 0
 
   // Finish: full row sums, then normalised bf16 output or a split-K partial.
   float lsum[2];
@@ -731,12 +758,10 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
     const float lp = l[nt][0] + l[nt][1];
     lsum[nt] = lp + swap_halves(lp);
   }
-  if (it.grow >= 0 && p.chunks > 1) {
-    const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.chunks + it.chunk;
-    float *part = p.ws + pidx * kPartialFloats;
-    // The 64 x 64 fp32 tile is staged in LDS (all four K/V buffers) so that
-    // the stores are whole 256-byte rows: 16-byte chunk k of row q sits at
-    // chunk k ^ (q & 15) of the LDS row.
+  if (it.grow >= 0) {
+    // Full-row chunk: each wavefront leaves its unnormalised 64 x 64 fp32
+    // tile in its own region (16-byte chunk k of row q at chunk k ^ (q & 15)
+    // of the 256-byte LDS row) and its row maxima and sums in merge_ml.
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -747,20 +772,50 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
           const int q = 32 * nt + c, k = 8 * dt + 2 * jj + h;
           *(f32x4 *)(lds + q * 256 + 16 * (k ^ (q & 15))) = y;
         }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS (one wavefront per workgroup)
-    {
-      const int k = lane & 15;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = 4 * i + (lane >> 4);
-        *(f32x4 *)(part + q * kD + 4 * k) = *(const f32x4 *)(lds + q * 256 + 16 * (k ^ (q & 15)));
-      }
-    }
     if (h == 0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        part[kQT * kD + 32 * nt + c] = mref[nt];
-        part[kQT * kD + kQT + 32 * nt + c] = lsum[nt];
+        merge_ml[wv * 2 * kQT + 32 * nt + c] = mref[nt];
+        merge_ml[wv * 2 * kQT + kQT + 32 * nt + c] = lsum[nt];
+      }
+    }
+    __syncthreads();   // the kGroup wavefronts are the kGroup chunks of this row tile
+    // Wavefront wv merges rows 16 wv .. 16 wv + 15; lane: row r, d = 16 qd .. 16 qd + 15.
+    const int r = 16 * wv + (lane >> 2), qd = lane & 3;
+    float mi[kGroup], M = kInitMax;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      mi[i] = merge_ml[i * 2 * kQT + r];
+      M = __builtin_fmaxf(M, mi[i]);
+    }
+    float den = 0.0f;
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const float w = __builtin_amdgcn_exp2f(mi[i] - M);
+      den += w * merge_ml[i * 2 * kQT + kQT + r];
+      const unsigned char *trow = lds_all + i * kWaveLds + r * 256;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] += w * *(const f32x4 *)(trow + 16 * ((4 * qd + t) ^ (r & 15)));
+    }
+    if (p.nparts == 1) {
+      const float inv = 1.0f / den;
+      bf16_t *orow = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)(q0 + r) * kD + 16 * qd;
+      const bf16x8 v0 = __builtin_shufflevector(__builtin_convertvector(acc[0] * inv, bf16x4),
+                                                __builtin_convertvector(acc[1] * inv, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 v1 = __builtin_shufflevector(__builtin_convertvector(acc[2] * inv, bf16x4),
+                                                __builtin_convertvector(acc[3] * inv, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+      __builtin_nontemporal_store(v0, (bf16x8 *)orow);
+      __builtin_nontemporal_store(v1, (bf16x8 *)(orow + 8));
+    } else {
+      // A partial over this group of chunks for the merge kernel.
+      const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.nparts + it.chunk / kGroup;
+      float *part = p.ws + pidx * kPartialFloats;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) *(f32x4 *)(part + r * kD + 16 * qd + 4 * t) = acc[t];
+      if (qd == 0) {
+        part[kQT * kD + r] = M;
+        part[kQT * kD + kQT + r] = den;
       }
     }
     return;
@@ -783,7 +838,7 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
         }
     }
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS (one wavefront per workgroup)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in this wavefront's own LDS region
   {
     bf16_t *out = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
     const int ch = lane & 7;
@@ -803,9 +858,9 @@ __global__ __launch_bounds__(64, 2) void bbsa_attn_bf16(Params p) {
 // steps over (mt, i) with key 16mt + 4g + i, read straight from memory.
 template <bool HAS_MASK>
 __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
-  const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x());
+  const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x(), 0);
   if (it.bh >= p.bh_total) return;
-  const int lane = (int)__builtin_amdgcn_workitem_id_x(), c = lane & 15, g = lane >> 4;
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
   const int b = fdiv(it.bh, p.div_heads);
   const float *Q = (const float *)p.q + (int64_t)it.bh * p.seq_stride;
   const float *K = (const float *)p.k + (int64_t)it.bh * p.seq_stride;
@@ -920,7 +975,7 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const int t2 = idx / p.qtiles;
   const int grow = t2 % p.n_rows_global;
   const int bh = t2 / p.n_rows_global;
-  const float *base = p.ws + (int64_t)idx * p.chunks * kPartialFloats;
+  const float *base = p.ws + (int64_t)idx * p.nparts * kPartialFloats;
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int q = 4 * slice + (tid >> 4), dq = tid & 15;
   // One pass, kMergeBatch chunks at a time: all loads of a batch are issued
@@ -928,12 +983,12 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   // batch raises the maximum.
   float M = kInitMax, den = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < p.chunks; c0 += kMergeBatch) {
+  for (int c0 = 0; c0 < p.nparts; c0 += kMergeBatch) {
     float mc[kMergeBatch], lc[kMergeBatch];
     f32x4 oc[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int ch = min(c0 + u, p.chunks - 1);   // repeats stay unused
+      const int ch = min(c0 + u, p.nparts - 1);   // repeats stay unused
       const float *part = base + (int64_t)ch * kPartialFloats;
       mc[u] = part[kQT * kD + q];
       lc[u] = part[kQT * kD + kQT + q];
@@ -942,13 +997,13 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
     float Mb = M;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      if (c0 + u < p.chunks) Mb = __builtin_fmaxf(Mb, mc[u]);
+      if (c0 + u < p.nparts) Mb = __builtin_fmaxf(Mb, mc[u]);
     const float r = __builtin_amdgcn_exp2f(M - Mb);
     den *= r;
     acc *= r;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float w = (c0 + u < p.chunks) ? __builtin_amdgcn_exp2f(mc[u] - Mb) : 0.0f;
+      const float w = (c0 + u < p.nparts) ? __builtin_amdgcn_exp2f(mc[u] - Mb) : 0.0f;
       den += w * lc[u];
       acc += w * oc[u];
     }
@@ -1030,19 +1085,29 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   p.B = B; p.H = H; p.L = L; p.nb = nb; p.block = block; p.r = r;
   p.qtiles = block / kQT;
   p.n_rows_global = full ? nb : 2;
-  // Full rows are cut into chunks (1024 keys for bf16, 256 for the slower
-  // fp32 path) so they do not form the tail.
-  p.chunk_blocks = (dtype == BBSA_F32 ? 256 : 1024) / block;
-  if (p.chunk_blocks > nb) p.chunk_blocks = nb;
-  p.chunks = (nb + p.chunk_blocks - 1) / p.chunk_blocks;
+  // Full rows are cut into chunks of about 1024 keys (bf16) or 256 keys (the
+  // slower fp32 path) so they do not form the tail.  On the bf16 path the
+  // chunk count is a multiple of kGroup: each workgroup runs kGroup chunks
+  // of one row tile and merges them in LDS, and the merge kernel combines
+  // the chunks / kGroup group results (none for rows of up to 4096 keys).
+  const int per_chunk = (dtype == BBSA_F32 ? 256 : 1024) / block;   // blocks
+  if (dtype == BBSA_BF16) {
+    p.group = kGroup;
+    p.chunks = kGroup * ((nb + kGroup * per_chunk - 1) / (kGroup * per_chunk));
+  } else {
+    p.group = 1;
+    p.chunks = (nb + per_chunk - 1) / per_chunk;
+  }
+  p.nparts = p.chunks / p.group;
   p.n_global_items = p.n_rows_global * p.qtiles * p.chunks;
   const int n_middle = full ? 0 : (nb - 2) * p.qtiles;
   const int64_t bh = (int64_t)B * H;
   const int64_t items_per_bh = (int64_t)p.n_global_items + n_middle;
   p.xcd_remap = bh >= 8 ? 1 : 0;
-  const int64_t grid = p.xcd_remap ? 8 * ((bh + 7) / 8) * items_per_bh : bh * items_per_bh;
-  const int64_t n_partials = (p.chunks > 1) ? bh * p.n_rows_global * p.qtiles * p.chunks : 0;
-  if (grid > 0x7fffffff || bh > 0x7fffffff || (int64_t)B * H * L * kD > ((int64_t)1 << 40) ||
+  const int64_t items_per_lane = (p.xcd_remap ? (bh + 7) / 8 : bh) * items_per_bh;
+  const int64_t grid = (p.xcd_remap ? 8 : 1) * ((items_per_lane + p.group - 1) / p.group);
+  const int64_t n_partials = (p.nparts > 1) ? bh * p.n_rows_global * p.qtiles * p.nparts : 0;
+  if (items_per_lane > 0x7fffffff || grid > 0x7fffffff || bh > 0x7fffffff || (int64_t)B * H * L * kD > ((int64_t)1 << 40) ||
       (int64_t)kMergeSlices * bh * p.n_rows_global * p.qtiles > 0x7fffffff)
     return BBSA_ERR_UNSUPPORTED;
   p.items_per_bh = (int)items_per_bh;
@@ -1062,7 +1127,7 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   const bool timed = g_timing.enabled && g_timing.n < kMaxTimed;
   const int tslot = g_timing.n;
   if (timed && hipEventRecord(g_timing.ev[tslot][0], stream) != hipSuccess) return BBSA_ERR_HIP;
-  const dim3 g1((unsigned)grid), b1(64);
+  const dim3 g1((unsigned)grid), b1(64 * p.group);
   if (dtype == BBSA_BF16) {
     if (mask) hipLaunchKernelGGL(bbsa_attn_bf16<true>, g1, b1, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_attn_bf16<false>, g1, b1, 0, stream, p);
