@@ -35,7 +35,9 @@
  *
  * Ownership: the caller owns every buffer it passes; the library never frees
  * caller memory.  The library owns one split-K workspace per device (grown on
- * demand with hipMalloc, released by bbsa_release_workspace).
+ * demand with hipMalloc, released by bbsa_release_workspace); it is used only
+ * when a full row needs more than one partial (bf16 rows longer than 4096
+ * keys at block 64, and the fp32 path).
  *
  * Errors: every function returns a status code (below); no C++ exception
  * crosses this interface.  Argument checks run on the host before any HIP
@@ -134,7 +136,8 @@ int bbsa_version(void);
 /*
  * Kernel timing for benchmarks.  When enabled, bbsa_forward records a pair of
  * HIP events on `stream` around its main attention kernel and around its
- * split-K combine kernel.  bbsa_timing_read synchronises on the recorded
+ * split-K combine kernel when one runs (combine_ms counts 0 otherwise).
+ * bbsa_timing_read synchronises on the recorded
  * events, returns the summed durations in milliseconds and the number of
  * timed calls, then clears the record.  At most 4096 calls are recorded
  * between reads; later calls are not timed.
