@@ -29,10 +29,10 @@ SMALL = [
     (2, 3, 1024, 64, 3, "bf16", (700, 1024), 1),
     (1, 2, 768, 64, 3, "bf16", None, 2),          # smallest sparse length at r=3 (nb = 12)
     (1, 2, 2048, 128, 2, "bf16", (1900,), 3),      # block 128, partial block
-    (2, 2, 4096, 64, 3, "bf16", (3072, 4000), 4),  # full rows split into 2 chunks
+    (2, 2, 4096, 64, 3, "bf16", (3072, 4000), 4),  # full rows: four chunks merged in one workgroup
     (1, 3, 1536, 64, 1, "bf16", None, 5),
     (1, 2, 2560, 64, 5, "bf16", (2000,), 6),
-    (1, 1, 5120, 128, 3, "bf16", (4321,), 7),      # block 128, 40 blocks, chunked full rows
+    (1, 1, 5120, 128, 3, "bf16", (4321,), 7),      # block 128, 40 blocks: 8 chunks, two groups + merge kernel
     (1, 2, 1024, 64, 3, "f32", None, 8),
     (2, 1, 2048, 128, 2, "f32", (1500, 2048), 9),
     (1, 2, 4096, 64, 2, "f32", (3333,), 10),
@@ -55,6 +55,12 @@ FALLBACK = [
     (2, 1, 1152, 128, 2, "bf16", None),    # (5 + 2*2) * 128
     (1, 1, 2880, 64, 20, "bf16", (2800,)), # 45 blocks: full rows are chunked and merged
     (1, 2, 448, 64, 1, "f32", None),
+    # Rows shorter than four blocks: some of the four chunks of a row are empty.
+    (1, 2, 64, 64, 1, "bf16", None),
+    (2, 1, 128, 64, 1, "bf16", (100, 128)),
+    (1, 1, 192, 64, 2, "bf16", None),
+    (1, 2, 256, 128, 1, "bf16", (200,)),
+    (1, 1, 128, 64, 1, "f32", None),
 ]
 
 
