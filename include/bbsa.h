@@ -37,7 +37,7 @@
  * caller memory.  The library owns one split-K workspace per device (grown on
  * demand with hipMalloc, released by bbsa_release_workspace); it is used only
  * when a full row needs more than one partial (bf16 rows longer than 4096
- * keys at block 64, and the fp32 path).
+ * keys, and fp32 rows longer than 256 keys).
  *
  * Errors: every function returns a status code (below); no C++ exception
  * crosses this interface.  Argument checks run on the host before any HIP
@@ -114,11 +114,13 @@ int bbsa_check_rand_attn(const int32_t *rand_attn, int H, int nb, int r);
  *
  * Returns BBSA_OK, or BBSA_OK_FULL_FALLBACK when L <= (5 + 2r) * block (every
  * query block then attends every key block), or a negative error code.  All
- * argument checks happen before any HIP call.  The library-owned workspace is
+ * argument checks happen before any HIP call.  The library-owned workspace
+ * (used only when a full row needs more than one partial, see above) is
  * allocated or grown on first use for a shape, which synchronises the
- * device; calls that overlap on one device through different streams must
- * not race on it (the library serialises its own bookkeeping with a mutex,
- * not the kernels).
+ * device; such calls that overlap on one device through different streams
+ * must not race on it (the library serialises its own bookkeeping with a
+ * mutex, not the kernels).  Calls that need no workspace (bf16 with
+ * L <= 4096) share nothing.
  */
 int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
                  const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
