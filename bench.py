@@ -55,13 +55,14 @@ def algorithmic_bytes(B, H, L, d, nb, r, elt) -> float:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source with comments and blank lines dropped, so that
-    a counter summary stays valid across comment-only edits."""
+    """Hash of the kernel source with comments, blank lines and indentation
+    dropped, so that a counter summary stays valid across comment-only and
+    formatting-only edits."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             for line in f:
-                code = line.split("//", 1)[0].rstrip()
+                code = line.split("//", 1)[0].strip()
                 if code:
                     h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]

@@ -624,132 +624,132 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
     // An empty key chunk (a row shorter than kGroup blocks): a neutral partial.
     mref[0] = mref[1] = kInitMax;
   } else {
-  // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
-  // bias is added at the top of the iteration that takes its softmax.
-  const int key_0 = key_of(0), key_1 = key_of(1);
-  float mk_cur = load_mask(key_0);            // mask of step j (j = 0)
-  dma_k(key_0, 0);
-  float mk_next = load_mask(key_1);           // mask of step j + 1
-  dma_k(key_1, 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  merge_plan(p, walk, rnd, rslot);
-  f32x16 sc[2];
-  {
-    bf16x8 kc[4];
-    read_k(0, kc);
-    sc[0] = score_half(kc, 0);
-    sc[1] = score_half(kc, 1);
-  }
-
-  bf16x8 pf[2][2];    // P of the previous step: [nt][key step s]
-  bool resc_pending = false;
-  float alpha_pending[2] = {1.0f, 1.0f};
-  // One pipeline iteration j: the PV product of step j-1, the softmax of step
-  // j (in sc) and S(j+1), computed half by half into the registers the
-  // softmax of that half has just consumed.
-  auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t, auto steady_t) {
-    constexpr bool HAS_S = decltype(has_s_t)::value;
-    constexpr bool HAS_PV = decltype(has_pv_t)::value;
-    constexpr bool FIRST = decltype(first_t)::value;
-    constexpr bool STEADY = decltype(steady_t)::value;   // j + 2 < n
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K(j+1), V(j-1), mask(j+2) from iteration j-1
-    bf16x8 kc[4], vt[2][2];
-    if (HAS_S) read_k((j + 1) & 1, kc);
-    if (HAS_PV) read_vt((j - 1) & 1, vt);
-    apply_mask(sc, mk_cur);
-    float mk_n2 = 1.0f;
-    if (STEADY || j + 2 < n) {
-      const int kk0 = key_of(j + 2);
-      mk_n2 = load_mask(kk0);
-      dma_k(kk0, j & 1);
+    // Prologue: K(0), K(1) and their mask values; S(0).  Each step's padding
+    // bias is added at the top of the iteration that takes its softmax.
+    const int key_0 = key_of(0), key_1 = key_of(1);
+    float mk_cur = load_mask(key_0);            // mask of step j (j = 0)
+    dma_k(key_0, 0);
+    float mk_next = load_mask(key_1);           // mask of step j + 1
+    dma_k(key_1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    merge_plan(p, walk, rnd, rslot);
+    f32x16 sc[2];
+    {
+      bf16x8 kc[4];
+      read_k(0, kc);
+      sc[0] = score_half(kc, 0);
+      sc[1] = score_half(kc, 1);
     }
-    dma_v(key_of(j), j & 1);
 
-    // A rescale decided in the previous iteration applies to O now: after the
-    // PV product of step j-2 and before that of step j-1 (whose probabilities
-    // already use the new reference).
+    bf16x8 pf[2][2];    // P of the previous step: [nt][key step s]
+    bool resc_pending = false;
+    float alpha_pending[2] = {1.0f, 1.0f};
+    // One pipeline iteration j: the PV product of step j-1, the softmax of step
+    // j (in sc) and S(j+1), computed half by half into the registers the
+    // softmax of that half has just consumed.
+    auto iteration = [&](int j, auto has_s_t, auto has_pv_t, auto first_t, auto steady_t) {
+      constexpr bool HAS_S = decltype(has_s_t)::value;
+      constexpr bool HAS_PV = decltype(has_pv_t)::value;
+      constexpr bool FIRST = decltype(first_t)::value;
+      constexpr bool STEADY = decltype(steady_t)::value;   // j + 2 < n
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K(j+1), V(j-1), mask(j+2) from iteration j-1
+      bf16x8 kc[4], vt[2][2];
+      if (HAS_S) read_k((j + 1) & 1, kc);
+      if (HAS_PV) read_vt((j - 1) & 1, vt);
+      apply_mask(sc, mk_cur);
+      float mk_n2 = 1.0f;
+      if (STEADY || j + 2 < n) {
+        const int kk0 = key_of(j + 2);
+        mk_n2 = load_mask(kk0);
+        dma_k(kk0, j & 1);
+      }
+      dma_v(key_of(j), j & 1);
+
+      // A rescale decided in the previous iteration applies to O now: after the
+      // PV product of step j-2 and before that of step j-1 (whose probabilities
+      // already use the new reference).
+      if (resc_pending) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha_pending[nt];
+        resc_pending = false;
+      }
+      // Rescale decision for step j (before its exponentials).
+      {
+        float ml[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          ml[nt] = tree_max16(sc[nt]) * kLog2e - mref[nt];
+        const bool need = FIRST || ml[0] > kTauLog2 || ml[1] > kTauLog2;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const float mrow = __builtin_fmaxf(ml[nt], swap_halves(ml[nt]));
+            const float sh = (FIRST || mrow > kTauLog2) ? mrow : 0.0f;
+            mref[nt] += sh;
+            alpha_pending[nt] = __builtin_amdgcn_exp2f(-sh);
+            if (!FIRST) {
+              l[nt][0] *= alpha_pending[nt];
+              l[nt][1] *= alpha_pending[nt];
+            }
+          }
+          // The first step has no O to rescale.
+          resc_pending = !FIRST;
+        }
+      }
+
+      if (HAS_PV) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
+      }
+      softmax_half(sc[0], 0, pf[0]);
+      if (HAS_S) sc[0] = score_half(kc, 0);
+      softmax_half(sc[1], 1, pf[1]);
+      if (HAS_S) sc[1] = score_half(kc, 1);
+      if (HAS_PV) {
+        BBSA_INTERLEAVE(8, 5);
+      }
+      if (HAS_S) {
+        BBSA_INTERLEAVE(4, 10);
+        BBSA_INTERLEAVE(4, 2);
+      }
+      mk_cur = mk_next;
+      mk_next = mk_n2;
+    };
+
+    using T = std::true_type;
+    using F = std::false_type;
+    iteration(0, T{}, F{}, T{}, F{});
+    int j = 1;
+    for (; j + 2 < n; ++j) iteration(j, T{}, T{}, F{}, T{});
+    for (; j < n - 1; ++j) iteration(j, T{}, T{}, F{}, F{});
+    iteration(n - 1, F{}, T{}, F{}, F{});
+    // Drain: PV of the last step.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (resc_pending) {
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha_pending[nt];
-      resc_pending = false;
     }
-    // Rescale decision for step j (before its exponentials).
     {
-      float ml[2];
+      bf16x8 vt[2][2];
+      read_vt((n - 1) & 1, vt);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        ml[nt] = tree_max16(sc[nt]) * kLog2e - mref[nt];
-      const bool need = FIRST || ml[0] > kTauLog2 || ml[1] > kTauLog2;
-      if (__builtin_amdgcn_ballot_w64(need)) {
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float mrow = __builtin_fmaxf(ml[nt], swap_halves(ml[nt]));
-          const float sh = (FIRST || mrow > kTauLog2) ? mrow : 0.0f;
-          mref[nt] += sh;
-          alpha_pending[nt] = __builtin_amdgcn_exp2f(-sh);
-          if (!FIRST) {
-            l[nt][0] *= alpha_pending[nt];
-            l[nt][1] *= alpha_pending[nt];
-          }
-        }
-        // The first step has no O to rescale.
-        resc_pending = !FIRST;
-      }
-    }
-
-    if (HAS_PV) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int s = 0; s < 2; ++s)
             o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
     }
-    softmax_half(sc[0], 0, pf[0]);
-    if (HAS_S) sc[0] = score_half(kc, 0);
-    softmax_half(sc[1], 1, pf[1]);
-    if (HAS_S) sc[1] = score_half(kc, 1);
-    if (HAS_PV) {
-      BBSA_INTERLEAVE(8, 5);
-    }
-    if (HAS_S) {
-      BBSA_INTERLEAVE(4, 10);
-      BBSA_INTERLEAVE(4, 2);
-    }
-    mk_cur = mk_next;
-    mk_next = mk_n2;
-  };
-
-  using T = std::true_type;
-  using F = std::false_type;
-  iteration(0, T{}, F{}, T{}, F{});
-  int j = 1;
-  for (; j + 2 < n; ++j) iteration(j, T{}, T{}, F{}, T{});
-  for (; j < n - 1; ++j) iteration(j, T{}, T{}, F{}, F{});
-  iteration(n - 1, F{}, T{}, F{}, F{});
-  // Drain: PV of the last step.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (resc_pending) {
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha_pending[nt];
   }
-  {
-    bf16x8 vt[2][2];
-    read_vt((n - 1) & 1, vt);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[dt][s], pf[nt][s], o[dt][nt], 0, 0, 0);
-  }
-  }   // n > 0
 
   // Finish: full row sums, then normalised bf16 output or a split-K partial.
   float lsum[2];
