@@ -171,10 +171,14 @@ __device__ inline float group4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Online-softmax state of the 4 query columns a lane holds (one per 16-query tile nt).
+// fp32 path: each wavefront owns kNT 16-query tiles of its item.
+constexpr int kNT = 1;
+constexpr int kF32Waves = 4 / kNT;   // wavefronts per fp32 workgroup (one item)
+
+// Online-softmax state of the kNT query columns a lane holds (one per 16-query tile nt).
 struct SoftmaxState {
-  float m[4];   // reference max (raw score units), identical across the 4 lane groups
-  float l[4];   // per-lane partial row sum of exp2 values
+  float m[kNT];   // reference max (raw score units), identical across the 4 lane groups
+  float l[kNT];   // per-lane partial row sum of exp2 values
 };
 
 // Lazy rescale for one 32-key step.  s[mt][nt][i] holds the score of key
@@ -183,11 +187,11 @@ struct SoftmaxState {
 // reference max + tau; only if some score exceeds it anywhere in the
 // wavefront is the full row max formed across the 4 lane groups and the
 // reference moved (for the queries that need it).
-__device__ inline void softmax_rescale(f32x4 (&s)[2][4], SoftmaxState &st, f32x4 (&o)[4][4]) {
-  float mloc[4];
+__device__ inline void softmax_rescale(f32x4 (&s)[2][kNT], SoftmaxState &st, f32x4 (&o)[4][kNT]) {
+  float mloc[kNT];
   bool need = false;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
     float a = __builtin_fmaxf(__builtin_fmaxf(s[0][nt][0], s[0][nt][1]), s[0][nt][2]);
     a = __builtin_fmaxf(__builtin_fmaxf(a, s[0][nt][3]), s[1][nt][0]);
     a = __builtin_fmaxf(__builtin_fmaxf(a, s[1][nt][1]), s[1][nt][2]);
@@ -196,7 +200,7 @@ __device__ inline void softmax_rescale(f32x4 (&s)[2][4], SoftmaxState &st, f32x4
   }
   if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
       const float mrow = group4_max(mloc[nt]);
       const bool up = mrow > st.m[nt] + kTau;
       const float alpha = up ? __builtin_amdgcn_exp2f((st.m[nt] - mrow) * kLog2e) : 1.0f;
@@ -209,9 +213,9 @@ __device__ inline void softmax_rescale(f32x4 (&s)[2][4], SoftmaxState &st, f32x4
 }
 
 // p = exp2((s - m) * log2 e) in place (unnormalised probabilities).
-__device__ inline void softmax_exp(f32x4 (&s)[2][4], const SoftmaxState &st) {
+__device__ inline void softmax_exp(f32x4 (&s)[2][kNT], const SoftmaxState &st) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
     const float nm = -st.m[nt] * kLog2e;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -222,9 +226,9 @@ __device__ inline void softmax_exp(f32x4 (&s)[2][4], const SoftmaxState &st) {
 }
 
 // Lane-partial row sums of fp32 probabilities.
-__device__ inline void row_sum_f32(const f32x4 (&s)[2][4], SoftmaxState &st) {
+__device__ inline void row_sum_f32(const f32x4 (&s)[2][kNT], SoftmaxState &st) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
     float acc = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -235,7 +239,7 @@ __device__ inline void row_sum_f32(const f32x4 (&s)[2][4], SoftmaxState &st) {
 }
 
 // Add the key-side padding bias to every score when any key of this step is padded.
-__device__ inline void apply_mask(f32x4 (&s)[2][4], const f32x4 (&mk)[2]) {
+__device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2]) {
   float bias[2][4];
   bool any = false;
 #pragma unroll
@@ -249,7 +253,7 @@ __device__ inline void apply_mask(f32x4 (&s)[2][4], const f32x4 (&mk)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[mt][nt][i] += bias[mt][i];
   }
@@ -336,34 +340,34 @@ __device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
 // Finish an item of the fp32 path: either normalise and store the output rows, or store a
 // split-K partial (unnormalised O, reference max, row sum).
 template <typename OutT>
-__device__ inline void finish_item(const Params &p, const Item &it, int q0, SoftmaxState &st,
-                                   f32x4 (&o)[4][4]) {
-  const int lane = (int)__builtin_amdgcn_workitem_id_x(), c = lane & 15, g = lane >> 4;
-  float lsum[4];
+__device__ inline void finish_item(const Params &p, const Item &it, int q0, int nt0, SoftmaxState &st,
+                                   f32x4 (&o)[4][kNT]) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  float lsum[kNT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) lsum[nt] = group4_sum(st.l[nt]);
+  for (int nt = 0; nt < kNT; ++nt) lsum[nt] = group4_sum(st.l[nt]);
   if (it.grow >= 0 && p.nparts > 1) {
     const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.nparts + it.chunk;
     float *part = p.ws + pidx * kPartialFloats;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        *(f32x4 *)(part + (16 * nt + c) * kD + 16 * dt + 4 * g) = o[dt][nt];
+        *(f32x4 *)(part + (16 * (nt0 + nt) + c) * kD + 16 * dt + 4 * g) = o[dt][nt];
     if (g == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        part[kQT * kD + 16 * nt + c] = st.m[nt] * kLog2e;   // log2 units
-        part[kQT * kD + kQT + 16 * nt + c] = lsum[nt];
+      for (int nt = 0; nt < kNT; ++nt) {
+        part[kQT * kD + 16 * (nt0 + nt) + c] = st.m[nt] * kLog2e;   // log2 units
+        part[kQT * kD + kQT + 16 * (nt0 + nt) + c] = lsum[nt];
       }
     }
     return;
   }
   OutT *out = (OutT *)p.out + (int64_t)it.bh * p.seq_stride;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
     const float inv = 1.0f / lsum[nt];
-    OutT *row = out + (int64_t)(q0 + 16 * nt + c) * kD;
+    OutT *row = out + (int64_t)(q0 + 16 * (nt0 + nt) + c) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const f32x4 y = o[dt][nt] * inv;
@@ -380,7 +384,7 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, Soft
 //
 // LDS per wavefront: two K tiles and two V tiles of 32 keys x 64 d bf16,
 // row-major (128 B per key row).  Tiles are filled straight from HBM with
-// global_load_lds_dwordx4: lane l of instruction u writes the 16 bytes at
+// buffer_load_dwordx4 ... lds: lane l of instruction u writes the 16 bytes at
 // tile + 1024u + 16l (key row 8u + l/8, chunk position l%8).  The 16-byte
 // chunk j of key row k is stored at position j ^ f(k):
 //   K: f(k) = ((k >> 1) & 7) ^ ((k & 1) << 2) -- the 16-byte A-operand reads
@@ -853,13 +857,19 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
 
 // ---------------------------------------------------------------- fp32 path
 //
-// Same walk and softmax on MFMA 16x16x4 f32.  The d contraction uses the
-// order d = 16g + s (s = MFMA step) on both operands; the PV contraction
-// steps over (mt, i) with key 16mt + 4g + i, read straight from memory.
+// Same walk and softmax on MFMA 16x16x4 f32, one item per workgroup of
+// kF32Waves wavefronts that split its query rows (all read the same K and V
+// rows, which the later wavefronts find in the caches).  The d contraction
+// uses the order d = 16g + s (s = MFMA step) on both operands; the PV
+// contraction steps over (mt, i) with key 16mt + 4g + i, read straight from
+// memory.
 template <bool HAS_MASK>
-__global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
+__global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
   const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x(), 0);
   if (it.bh >= p.bh_total) return;
+  // The kF32Waves wavefronts of a workgroup split the item's 64 query rows:
+  // wavefront wv owns the 16-query tiles nt0 .. nt0 + kNT - 1.
+  const int nt0 = kNT * __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_workitem_id_x() >> 6);
   const int lane = lane_id(), c = lane & 15, g = lane >> 4;
   const int b = fdiv(it.bh, p.div_heads);
   const float *Q = (const float *)p.q + (int64_t)it.bh * p.seq_stride;
@@ -868,12 +878,12 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
   const float *mrow = HAS_MASK ? p.mask + (int64_t)b * p.L : nullptr;
   const int q0 = it.qblock * p.block + it.qt * kQT;
 
-  float qf[4][16];
+  float qf[kNT][16];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const f32x4 x = *(const f32x4 *)(Q + (int64_t)(q0 + 16 * nt + c) * kD + 16 * g + 4 * s4);
+      const f32x4 x = *(const f32x4 *)(Q + (int64_t)(q0 + 16 * (nt0 + nt) + c) * kD + 16 * g + 4 * s4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf[nt][4 * s4 + e] = x[e];
     }
@@ -881,12 +891,12 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
   const KeyWalk walk = make_walk(p, it);
   SoftmaxState st;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) { st.m[nt] = kInitMax; st.l[nt] = 0.0f; }
-  f32x4 o[4][4];
+  for (int nt = 0; nt < kNT; ++nt) { st.m[nt] = kInitMax; st.l[nt] = 0.0f; }
+  f32x4 o[4][kNT];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kNT; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Operands of one step: K rows 16mt + c (d = 16g .. 16g+15) and the V
   // values of keys 16mt + 4g + i at d = c + 16dt.  The next step's are loaded
@@ -928,11 +938,11 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
       cur.advance(p, walk);
       load_step(cur.key0, nxt);
     }
-    f32x4 s[2][4];
+    f32x4 s[2][kNT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks)
@@ -953,10 +963,10 @@ __global__ __launch_bounds__(64) void bbsa_attn_f32(Params p) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
+          for (int nt = 0; nt < kNT; ++nt)
             o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.va[mt][i][dt], s[mt][nt][i], o[dt][nt], 0, 0, 0);
   }
-  finish_item<float>(p, it, q0, st, o);
+  finish_item<float>(p, it, q0, nt0, st, o);
 }
 
 // ---------------------------------------------------------------- split-K merge
@@ -1127,7 +1137,7 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   const bool timed = g_timing.enabled && g_timing.n < kMaxTimed;
   const int tslot = g_timing.n;
   if (timed && hipEventRecord(g_timing.ev[tslot][0], stream) != hipSuccess) return BBSA_ERR_HIP;
-  const dim3 g1((unsigned)grid), b1(64 * p.group);
+  const dim3 g1((unsigned)grid), b1(dtype == BBSA_BF16 ? 64 * p.group : 64 * kF32Waves);
   if (dtype == BBSA_BF16) {
     if (mask) hipLaunchKernelGGL(bbsa_attn_bf16<true>, g1, b1, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_attn_bf16<false>, g1, b1, 0, stream, p);
