@@ -337,6 +337,13 @@ __device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
   return w;
 }
 
+// The fp32 O^T accumulator o[dt][nt] holds, in lane (c, g) and register i,
+// d = 16g + 4i + dt of query 16 nt + c: the four d-tiles together give four
+// consecutive d.
+__device__ inline f32x4 d_run(const f32x4 (&o)[4][kNT], int nt, int i) {
+  return f32x4{o[0][nt][i], o[1][nt][i], o[2][nt][i], o[3][nt][i]};
+}
+
 // Finish an item of the fp32 path: either normalise and store the output rows, or store a
 // split-K partial (unnormalised O, reference max, row sum).
 template <typename OutT>
@@ -352,8 +359,8 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, int 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        *(f32x4 *)(part + (16 * (nt0 + nt) + c) * kD + 16 * dt + 4 * g) = o[dt][nt];
+      for (int i = 0; i < 4; ++i)
+        *(f32x4 *)(part + (16 * (nt0 + nt) + c) * kD + 16 * g + 4 * i) = d_run(o, nt, i);
     if (g == 0) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
@@ -369,12 +376,12 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, int 
     const float inv = 1.0f / lsum[nt];
     OutT *row = out + (int64_t)(q0 + 16 * (nt0 + nt) + c) * kD;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const f32x4 y = o[dt][nt] * inv;
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 y = d_run(o, nt, i) * inv;
       if constexpr (sizeof(OutT) == 2) {
-        *(bf16x4 *)(row + 16 * dt + 4 * g) = __builtin_convertvector(y, bf16x4);
+        *(bf16x4 *)(row + 16 * g + 4 * i) = __builtin_convertvector(y, bf16x4);
       } else {
-        *(f32x4 *)(row + 16 * dt + 4 * g) = y;
+        *(f32x4 *)(row + 16 * g + 4 * i) = y;
       }
     }
   }
@@ -899,8 +906,9 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
     for (int nt = 0; nt < kNT; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Operands of one step: K rows 16mt + c (d = 16g .. 16g+15) and the V
-  // values of keys 16mt + 4g + i at d = c + 16dt.  The next step's are loaded
-  // while the current one is computed.
+  // values of keys 16mt + 4g + i at d = 4c + dt (one 16-byte load per key:
+  // the PV product's d-tile dt holds the d = dt mod 4 columns).  The next
+  // step's are loaded while the current one is computed.
   struct StepOperands {
     float kf[2][16];
     float va[2][4][4];
@@ -917,9 +925,9 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float *vrow = V + (int64_t)(key0 + 16 * mt + 4 * g + i) * kD + c;
+        const f32x4 v4 = *(const f32x4 *)(V + (int64_t)(key0 + 16 * mt + 4 * g + i) * kD + 4 * c);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) x.va[mt][i][dt] = vrow[16 * dt];
+        for (int dt = 0; dt < 4; ++dt) x.va[mt][i][dt] = v4[dt];
       }
     }
     if (HAS_MASK) {
