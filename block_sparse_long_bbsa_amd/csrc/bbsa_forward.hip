@@ -9,14 +9,17 @@
 // additive -10000; each query row takes a softmax over the keys it attends.
 //
 // How it is computed here (the pages' five-segment einsum layout is not used):
-//   * one wavefront (one 64-thread workgroup) owns 64 query rows of one query
-//     block and walks the item's key blocks in steps of 32 keys;
+//   * a work item is 64 query rows of one query block against the key blocks
+//     of a middle row or one key chunk of a global row, walked in steps of
+//     32 keys; on the bf16 path one wavefront runs one item and a 256-thread
+//     workgroup runs four consecutive items, on the fp32 path the four
+//     wavefronts of a workgroup split one item's query rows;
 //   * bf16 path: scores are computed transposed, S^T = K Q^T, on MFMA
 //     32x32x16 bf16, so each lane holds 16 keys of one query column and the
 //     row max needs a single cross-lane swap; a probability costs one FMA
 //     (score * log2(e) - reference max) and one v_exp_f32;
-//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
-//     XOR-swizzled rows); K is read back as the MFMA A operand, V is read back
+//   * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ...
+//     lds, XOR-swizzled rows); K is read back as the MFMA A operand, V is read back
 //     transposed with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T;
 //     P is rounded to bf16 in registers and used directly as the B operand;
 //   * software pipeline: the softmax of step j runs between the MFMAs of
@@ -24,9 +27,10 @@
 //     ahead, V tiles one step ahead;
 //   * online softmax in base 2 with a lazy rescale (the reference max moves
 //     only when a score exceeds it by more than 8, i.e. p > 2^8);
-//   * the two global query blocks are split along the keys into chunks whose
-//     partials (O, max, sum) go to a workspace and are merged by a second
-//     kernel with the log-sum-exp rule;
+//   * the two global query blocks are split along the keys into chunks; on
+//     the bf16 path the four chunks of a workgroup merge their partials
+//     (O, max, sum) in LDS with the log-sum-exp rule, and longer rows (and
+//     the fp32 path) leave partials in a workspace for a second kernel;
 //   * workgroups are mapped onto the 8 XCDs so that all items of one
 //     (batch, head) run on one XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -402,14 +406,9 @@ constexpr int kTileBytes = kStep * kD * 2;          // 4 KB
 __device__ inline int k_swz(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 __device__ inline int v_swz(int row) { return ((row >> 1) & 1) << 2; }
 
-typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle, no stride.
 constexpr int kBufferWord3 = 0x00020000;
-
-__device__ inline void dma16(const void *src, unsigned char *lds_dst) {
-  __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_dst, 16, 0, 0);
-}
 
 // Scheduling hints: interleave `nmfma` MFMAs with `per` VALU instructions each.
 #define BBSA_INTERLEAVE(nmfma, per)                              \
