@@ -121,6 +121,12 @@ int bbsa_check_rand_attn(const int32_t *rand_attn, int H, int nb, int r);
  * must not race on it (the library serialises its own bookkeeping with a
  * mutex, not the kernels).  Calls that need no workspace (bf16 with
  * L <= 4096) share nothing.
+ *
+ * Graph capture: a call enqueues kernel launches only (no memset, no copy,
+ * no host synchronisation), so it can be recorded into a HIP graph once the
+ * workspace is large enough, e.g. after one eager call of the same shape;
+ * replays then reuse the captured pointers.  Kernel timing must be off
+ * during capture.
  */
 int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
                  const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
