@@ -101,6 +101,10 @@ struct Params {
   int chunks;                // key chunks per full row (block range [c nb / chunks, (c + 1) nb / chunks))
   int group;                 // items per workgroup: 4 on the bf16 path (a full row's chunks in fours), else 1
   int nparts;                // split-K partials per full row left for the merge kernel: chunks / group
+  int mparts;                // key parts per middle row (fp32 path with few items: 2; else 1)
+  int comb_rows_global;      // per (batch, head): full rows the merge kernel combines (0 or n_rows_global)
+  int comb_rows_mid;         // per (batch, head): middle rows the merge kernel combines (0 or nb - 2)
+  int64_t mid_part_base;     // index of the first middle-row partial in the workspace
   int n_global_items;        // per (batch, head): n_rows_global * qtiles * chunks
   int items_per_bh;          // n_global_items + middle items
   int bh_total;              // B * H
@@ -111,6 +115,7 @@ struct Params {
   FastDiv div_row;           // qtiles * chunks
   FastDiv div_chunks;        // chunks
   FastDiv div_qtiles;        // qtiles
+  FastDiv div_mparts;        // mparts
   FastDiv div_heads;         // H
 };
 
@@ -122,7 +127,7 @@ struct Item {
   int qblock;
   int qt;
   int grow;       // full-row index (partials), -1 for a middle row
-  int chunk;      // key chunk of a full row
+  int chunk;      // key chunk of a full row, or key part of a middle row
 };
 
 // Workgroup -> item.  Workgroups are dispatched in index order, so the
@@ -151,12 +156,13 @@ __device__ inline Item decode_item(const Params &p, int wg, int wv) {
   const int grow = fdiv(lr, p.div_row);
   const int rem = lr - grow * (int)p.div_row.d;
   const int qt_g = fdiv(rem, p.div_chunks);
-  const int mq = fdiv(m, p.div_qtiles);
+  const int mp = fdiv(m, p.div_mparts);   // middle item m = key part + mparts * (query tile + qtiles * row)
+  const int mq = fdiv(mp, p.div_qtiles);
   Item it;
   it.bh = bh;   // >= bh_total marks an idle workgroup
   it.grow = global_row ? grow : -1;
-  it.qt = global_row ? qt_g : m - mq * p.qtiles;
-  it.chunk = global_row ? rem - qt_g * p.chunks : 0;
+  it.qt = global_row ? qt_g : mp - mq * p.qtiles;
+  it.chunk = global_row ? rem - qt_g * p.chunks : m - mp * p.mparts;
   it.qblock = global_row ? ((p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow) : 1 + mq;
   return it;
 }
@@ -178,6 +184,12 @@ __device__ inline float group4_sum(float x) {
 // fp32 path: each wavefront owns kNT 16-query tiles of its item.
 constexpr int kNT = 1;
 constexpr int kF32Waves = 4 / kNT;   // wavefronts per fp32 workgroup (one item)
+// Below this many wavefronts (about two per SIMD) the fp32 path cuts its work
+// finer: full-row chunks of kF32SmallChunkKeys keys, middle rows in
+// kF32SmallParts key parts.
+constexpr int64_t kF32SplitBelowWaves = 2048;
+constexpr int kF32SmallChunkKeys = 128;
+constexpr int kF32SmallParts = 4;
 
 // Online-softmax state of the kNT query columns a lane holds (one per 16-query tile nt).
 struct SoftmaxState {
@@ -280,6 +292,12 @@ struct WalkCursor {
     sb = 0;
     key0 = __builtin_amdgcn_readfirstlane(w.first_blk * p.block);   // uniform; no plan entry needed
   }
+  // Start at position t0 of the block list (plan entries already merged).
+  __device__ inline void start_at(const Params &p, const KeyWalk &w, int t0) {
+    t = t0;
+    sb = 0;
+    key0 = __builtin_amdgcn_readlane(w.blk, t0) * p.block;
+  }
   __device__ inline void advance(const Params &p, const KeyWalk &w) {
     if (++sb == w.steps_per_block) {
       sb = 0;
@@ -357,8 +375,11 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, int 
   float lsum[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) lsum[nt] = group4_sum(st.l[nt]);
-  if (it.grow >= 0 && p.nparts > 1) {
-    const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.nparts + it.chunk;
+  const bool full_part = it.grow >= 0 && p.nparts > 1, mid_part = it.grow < 0 && p.mparts > 1;
+  if (full_part || mid_part) {
+    const int64_t pidx =
+        full_part ? (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.nparts + it.chunk
+                  : p.mid_part_base + (((int64_t)it.bh * (p.nb - 2) + (it.qblock - 1)) * p.qtiles + it.qt) * p.mparts + it.chunk;
     float *part = p.ws + pidx * kPartialFloats;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
@@ -935,13 +956,20 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
     }
   };
 
+  // A middle row split into key parts walks list positions [pos0, pos1).
+  int pos0 = 0, n_steps = walk.n_steps;
+  if (it.grow < 0 && p.mparts > 1) {
+    const int nblk = walk.n_steps / walk.steps_per_block;
+    pos0 = it.chunk * nblk / p.mparts;
+    n_steps = ((it.chunk + 1) * nblk / p.mparts - pos0) * walk.steps_per_block;
+  }
   WalkCursor cur;
-  cur.start(p, walk);
+  cur.start_at(p, walk, pos0);
   StepOperands nxt;
   load_step(cur.key0, nxt);
-  for (int step = 0; step < walk.n_steps; ++step) {
+  for (int step = 0; step < n_steps; ++step) {
     const StepOperands x = nxt;
-    if (step + 1 < walk.n_steps) {
+    if (step + 1 < n_steps) {
       cur.advance(p, walk);
       load_step(cur.key0, nxt);
     }
@@ -990,9 +1018,16 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const int slice = wg % kMergeSlices, idx = wg / kMergeSlices;
   const int qt = idx % p.qtiles;
   const int t2 = idx / p.qtiles;
-  const int grow = t2 % p.n_rows_global;
-  const int bh = t2 / p.n_rows_global;
-  const float *base = p.ws + (int64_t)idx * p.nparts * kPartialFloats;
+  const int rows = p.comb_rows_global + p.comb_rows_mid;
+  const int row = t2 % rows;
+  const int bh = t2 / rows;
+  // Full rows first (their chunk partials), then the middle rows' key parts.
+  const bool full_row = row < p.comb_rows_global;
+  const int i_mid = row - p.comb_rows_global;
+  const int np = full_row ? p.nparts : p.mparts;
+  const int64_t first = full_row ? (((int64_t)bh * p.n_rows_global + row) * p.qtiles + qt) * p.nparts
+                                 : p.mid_part_base + (((int64_t)bh * (p.nb - 2) + i_mid) * p.qtiles + qt) * p.mparts;
+  const float *base = p.ws + first * kPartialFloats;
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int q = 4 * slice + (tid >> 4), dq = tid & 15;
   // One pass, kMergeBatch chunks at a time: all loads of a batch are issued
@@ -1000,12 +1035,12 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   // batch raises the maximum.
   float M = kInitMax, den = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < p.nparts; c0 += kMergeBatch) {
+  for (int c0 = 0; c0 < np; c0 += kMergeBatch) {
     float mc[kMergeBatch], lc[kMergeBatch];
     f32x4 oc[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int ch = min(c0 + u, p.nparts - 1);   // repeats stay unused
+      const int ch = min(c0 + u, np - 1);   // repeats stay unused
       const float *part = base + (int64_t)ch * kPartialFloats;
       mc[u] = part[kQT * kD + q];
       lc[u] = part[kQT * kD + kQT + q];
@@ -1014,25 +1049,25 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
     float Mb = M;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      if (c0 + u < p.nparts) Mb = __builtin_fmaxf(Mb, mc[u]);
+      if (c0 + u < np) Mb = __builtin_fmaxf(Mb, mc[u]);
     const float r = __builtin_amdgcn_exp2f(M - Mb);
     den *= r;
     acc *= r;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float w = (c0 + u < p.nparts) ? __builtin_amdgcn_exp2f(mc[u] - Mb) : 0.0f;
+      const float w = (c0 + u < np) ? __builtin_amdgcn_exp2f(mc[u] - Mb) : 0.0f;
       den += w * lc[u];
       acc += w * oc[u];
     }
     M = Mb;
   }
   const f32x4 y = acc * (1.0f / den);
-  const int qblock = (p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow;
-  OutT *row = (OutT *)p.out + (int64_t)bh * p.seq_stride + (int64_t)(qblock * p.block + qt * kQT + q) * kD + 4 * dq;
+  const int qblock = full_row ? ((p.n_rows_global == 2) ? (row == 0 ? 0 : p.nb - 1) : row) : 1 + i_mid;
+  OutT *dst = (OutT *)p.out + (int64_t)bh * p.seq_stride + (int64_t)(qblock * p.block + qt * kQT + q) * kD + 4 * dq;
   if constexpr (sizeof(OutT) == 2) {
-    *(bf16x4 *)row = __builtin_convertvector(y, bf16x4);
+    *(bf16x4 *)dst = __builtin_convertvector(y, bf16x4);
   } else {
-    *(f32x4 *)row = y;
+    *(f32x4 *)dst = y;
   }
 }
 
@@ -1107,7 +1142,19 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   // chunk count is a multiple of kGroup: each workgroup runs kGroup chunks
   // of one row tile and merges them in LDS, and the merge kernel combines
   // the chunks / kGroup group results (none for rows of up to 4096 keys).
-  const int per_chunk = (dtype == BBSA_F32 ? 256 : 1024) / block;   // blocks
+  const int64_t bh = (int64_t)B * H;
+  int per_chunk = (dtype == BBSA_F32 ? 256 : 1024) / block;   // blocks
+  // The fp32 path has too few wavefronts for the chip when a call is small:
+  // then it cuts full rows into shorter chunks and middle rows into key parts
+  // (kF32SmallParts), all merged by the merge kernel.
+  bool f32_small = false;
+  if (dtype == BBSA_F32 && !full) {
+    const int64_t items = bh * p.qtiles * (2 * (int64_t)((nb + per_chunk - 1) / per_chunk) + (nb - 2));
+    if (items * kF32Waves < kF32SplitBelowWaves) {
+      f32_small = true;
+      per_chunk = std::max(1, kF32SmallChunkKeys / block);
+    }
+  }
   if (dtype == BBSA_BF16) {
     p.group = kGroup;
     p.chunks = kGroup * ((nb + kGroup * per_chunk - 1) / (kGroup * per_chunk));
@@ -1117,15 +1164,21 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   }
   p.nparts = p.chunks / p.group;
   p.n_global_items = p.n_rows_global * p.qtiles * p.chunks;
-  const int n_middle = full ? 0 : (nb - 2) * p.qtiles;
-  const int64_t bh = (int64_t)B * H;
+  p.mparts = f32_small ? kF32SmallParts : 1;
+  const int n_middle = full ? 0 : (nb - 2) * p.qtiles * p.mparts;
   const int64_t items_per_bh = (int64_t)p.n_global_items + n_middle;
   p.xcd_remap = bh >= 8 ? 1 : 0;
   const int64_t items_per_lane = (p.xcd_remap ? (bh + 7) / 8 : bh) * items_per_bh;
   const int64_t grid = (p.xcd_remap ? 8 : 1) * ((items_per_lane + p.group - 1) / p.group);
-  const int64_t n_partials = (p.nparts > 1) ? bh * p.n_rows_global * p.qtiles * p.nparts : 0;
+  const int64_t n_part_full = (p.nparts > 1) ? bh * p.n_rows_global * p.qtiles * p.nparts : 0;
+  const int64_t n_part_mid = (p.mparts > 1) ? bh * (nb - 2) * p.qtiles * p.mparts : 0;
+  const int64_t n_partials = n_part_full + n_part_mid;
+  p.mid_part_base = n_part_full;
+  p.comb_rows_global = (p.nparts > 1) ? p.n_rows_global : 0;
+  p.comb_rows_mid = (p.mparts > 1) ? nb - 2 : 0;
+  const int64_t comb_grid = (int64_t)kMergeSlices * bh * (p.comb_rows_global + p.comb_rows_mid) * p.qtiles;
   if (items_per_lane > 0x7fffffff || grid > 0x7fffffff || bh > 0x7fffffff || (int64_t)B * H * L * kD > ((int64_t)1 << 40) ||
-      (int64_t)kMergeSlices * bh * p.n_rows_global * p.qtiles > 0x7fffffff)
+      comb_grid > 0x7fffffff)
     return BBSA_ERR_UNSUPPORTED;
   p.items_per_bh = (int)items_per_bh;
   p.bh_total = (int)bh;
@@ -1135,6 +1188,7 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   p.div_row = make_fastdiv((uint32_t)(p.qtiles * p.chunks));
   p.div_chunks = make_fastdiv((uint32_t)p.chunks);
   p.div_qtiles = make_fastdiv((uint32_t)p.qtiles);
+  p.div_mparts = make_fastdiv((uint32_t)p.mparts);
   p.div_heads = make_fastdiv((uint32_t)H);
   if (n_partials > 0) {
     const int rc = ensure_workspace((size_t)n_partials * kPartialFloats * sizeof(float), &p.ws);
@@ -1156,7 +1210,7 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   if (timed && hipEventRecord(g_timing.ev[tslot][1], stream) != hipSuccess) return BBSA_ERR_HIP;
   if (n_partials > 0) {
     if (timed && hipEventRecord(g_timing.ev[tslot][2], stream) != hipSuccess) return BBSA_ERR_HIP;
-    const dim3 g2((unsigned)(kMergeSlices * bh * p.n_rows_global * p.qtiles)), b2(64);
+    const dim3 g2((unsigned)comb_grid), b2(64);
     if (dtype == BBSA_BF16) hipLaunchKernelGGL(bbsa_combine<bf16_t>, g2, b2, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_combine<float>, g2, b2, 0, stream, p);
     if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;

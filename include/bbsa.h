@@ -36,8 +36,9 @@
  * Ownership: the caller owns every buffer it passes; the library never frees
  * caller memory.  The library owns one split-K workspace per device (grown on
  * demand with hipMalloc, released by bbsa_release_workspace); it is used only
- * when a full row needs more than one partial (bf16 rows longer than 4096
- * keys, and fp32 rows longer than 256 keys).
+ * when a row needs more than one partial: bf16 rows longer than 4096 keys,
+ * fp32 rows longer than 256 keys, and, in fp32 calls with fewer than 2048
+ * wavefronts of work, full rows longer than 128 keys and every middle row.
  *
  * Errors: every function returns a status code (below); no C++ exception
  * crosses this interface.  Argument checks run on the host before any HIP

@@ -50,6 +50,19 @@ def test_small_full_compare(B, H, L, block, r, dtype, valid, seed):
     assert_close(got, want, dtype, f"small L{L}")
 
 
+
+def test_f32_large_call_without_middle_split():
+    # 1472 work items (5888 wavefronts): enough that the fp32 path leaves
+    # middle rows whole (smaller fp32 calls split them into two key parts).
+    announce("f32 without middle split B4 H8 L2048")
+    inp = workloads.make_case(4, 8, 2048, 64, 16, dtype="f32", valid=(2048, 1900, 1500, 2048))
+    cplan, oplan = plans(8, 32, 3, 16)
+    got, st = run_gpu(inp, 64, 3, "f32", cplan)
+    assert st == bbsa.BBSA_OK
+    blocks = sample_blocks(32)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64, query_blocks=blocks)
+    assert_close(gather_rows(got, blocks, 64), want, "f32", "f32 no split")
+
 FALLBACK = [
     (1, 2, 704, 64, 3, "bf16", (650,)),    # (5 + 2*3) * 64 = 704: full attention
     (2, 1, 1152, 128, 2, "bf16", None),    # (5 + 2*2) * 128
