@@ -1118,6 +1118,11 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
                             const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
                             void *out, hipStream_t stream, int dtype) {
   if (!q || !k || !v || !out) return BBSA_ERR_ARG;
+  // The kernels move q, k, v, out and the mask in 16-byte pieces.
+  auto misaligned = [](const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+      (mask && misaligned(mask, 16)) || (rand_attn && misaligned(rand_attn, 4)))
+    return BBSA_ERR_ARG;
   if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block <= 0 || r < 1) return BBSA_ERR_ARG;
   if (dtype != BBSA_BF16 && dtype != BBSA_F32) return BBSA_ERR_UNSUPPORTED;
   if (d != kD || (block != 64 && block != 128)) return BBSA_ERR_UNSUPPORTED;
@@ -1227,7 +1232,7 @@ extern "C" const char *bbsa_status_string(int status) {
   switch (status) {
     case BBSA_OK: return "ok";
     case BBSA_OK_FULL_FALLBACK: return "ok: sequence too short for the sparse pattern, computed full attention";
-    case BBSA_ERR_ARG: return "invalid argument (null pointer, non-positive size or r < 1)";
+    case BBSA_ERR_ARG: return "invalid argument (null or misaligned pointer, non-positive size or r < 1)";
     case BBSA_ERR_SHAPE: return "invalid shape (length not a multiple of the block, or nb < 5 + r)";
     case BBSA_ERR_UNSUPPORTED: return "unsupported configuration (d != 64, block not 64/128, dtype, or size)";
     case BBSA_ERR_HIP: return "HIP runtime error";

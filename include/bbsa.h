@@ -61,7 +61,7 @@ typedef enum { BBSA_BF16 = 0, BBSA_F32 = 1 } bbsa_dtype;
 enum {
   BBSA_OK = 0,               /* success */
   BBSA_OK_FULL_FALLBACK = 1, /* success; L <= (5+2r)*block, computed as full attention */
-  BBSA_ERR_ARG = -1,         /* null pointer, or B/H/L/d/block <= 0, or r < 1 */
+  BBSA_ERR_ARG = -1,         /* null or misaligned pointer, or B/H/L/d/block <= 0, or r < 1 */
   BBSA_ERR_SHAPE = -2,       /* L % block != 0, or nb < 5 + r where a plan is required */
   BBSA_ERR_UNSUPPORTED = -3, /* d != 64, block not in {64, 128}, unknown dtype, too large */
   BBSA_ERR_HIP = -4,         /* a HIP call or kernel launch failed */
@@ -97,7 +97,8 @@ int bbsa_check_rand_attn(const int32_t *rand_attn, int H, int nb, int r);
 /*
  * Block-sparse attention forward on `stream`.
  *
- * q, k, v:   device, [B, H, L, d] of `dtype`.
+ * q, k, v:   device, [B, H, L, d] of `dtype`, 16-byte aligned (as are out
+ *            and mask; rand_attn 4-byte aligned), else BBSA_ERR_ARG.
  * mask:      device float32 [B, L], 1 = valid key, 0 = padding (fractional
  *            values act through the bias -10000 * (1 - mask)); NULL = all
  *            keys valid.

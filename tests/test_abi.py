@@ -64,6 +64,10 @@ def call(lib, B=1, H=1, L=1024, d=64, block=64, r=3, dtype=0, q=FAKE, k=FAKE, v=
     (dict(d=128), -3), (dict(block=32, L=1024), -3), (dict(dtype=7), -3),
     (dict(B=1 << 20, H=1 << 10, L=1 << 14), -3),   # beyond the supported size
     (dict(L=8192, r=60), -3),                  # a middle row would list 65 key blocks
+    (dict(q=ctypes.c_void_p(0x1008)), -1),     # device pointers must be 16-byte aligned
+    (dict(out=ctypes.c_void_p(0x1004)), -1),
+    (dict(mask=ctypes.c_void_p(0x1008)), -1),
+    (dict(ra=ctypes.c_void_p(0x1002)), -1),    # the plan 4-byte aligned
 ])
 def test_forward_rejects_invalid_arguments(lib, kw, code):
     assert call(lib, **kw) == code
