@@ -11,6 +11,13 @@ previous one.  The JSON line also carries the 10th/50th/90th percentile of
 single steps each bracketed by its own events, and the warm-cache step time
 (the same input set every step) for comparison.
 
+The other workloads at L >= 4096 (Pegasus-large encoder shape, the 16384-token
+and the 32768-token block-128 cases) are timed in the same run with the same
+protocol and reported under ``config.other_workloads``.  Before each
+workload's warm-up steps a fixed wall time of untimed steps lets the GPU's
+clocks ramp up (``--preroll``; its length and step count are in the line).
+The roofline fractions are computed from the step time.
+
 Prints one JSON line on stdout; diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -81,41 +88,176 @@ def read_traffic(workload_name: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, plan, w, budget_s: float):
-    """Time the oracle on a bounded sample: whole (batch, head) slices of the
-    same workload, as many as fit in about ``budget_s`` seconds."""
-    import oracle
+def host_info():
+    """Host cores this process may run on, the CPU model and the BLAS threads."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas = 1
+    return cores, model, blas
+
+
+def cpu_baseline(inp, plan, w, budget_s: float):
+    """Time the oracle on a bounded sample: whole (batch, head) slices of the
+    same workload, as many as fit in about ``budget_s`` seconds.  The BLAS
+    pool is capped at the number of host cores this process may use, so
+    ``cores`` is both the host core count and the most threads the oracle
+    used."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    cores, model, blas = host_info()
     flops_per_slice = useful_flops(1, 1, w.nb, w.block, w.d, w.r)
     done, t0 = 0, time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            oracle.forward(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
-                           inp["v"][b:b + 1, h:h + 1], inp["mask"][b:b + 1], plan[h:h + 1], w.block)
-            done += 1
+    with threadpool_limits(cores):
+        for b in range(w.B):
+            for h in range(w.H):
+                oracle.forward(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
+                               inp["v"][b:b + 1, h:h + 1], inp["mask"][b:b + 1], plan[h:h + 1], w.block)
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
             if time.perf_counter() - t0 > budget_s:
                 break
-        if time.perf_counter() - t0 > budget_s:
-            break
     dt = time.perf_counter() - t0
-    return {"value": flops_per_slice * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": flops_per_slice * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "cpu_model": model, "blas_threads": int(min(blas, cores)),
             "sample": f"{done} of {w.B * w.H} (batch, head) slices of {w.name}, float64 dense "
                       f"masked attention, {dt:.1f} s wall"}
+
+
+def roofline(w, step_ms):
+    """Fractions of the MI355X roofs for one step of workload ``w`` taking
+    ``step_ms``: useful flops against the dtype's dense MFMA peak, algorithmic
+    bytes against HBM; the binding roof is the one with the longer time."""
+    elt = 2 if w.dtype == "bf16" else 4
+    flops = useful_flops(w.B, w.H, w.nb, w.block, w.d, w.r)
+    nbytes = algorithmic_bytes(w.B, w.H, w.L, w.d, w.nb, w.r, elt)
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_mfma = flops / (peak_mfma * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    sec = step_ms * 1e-3
+    mfma_frac = flops / sec / 1e12 / peak_mfma
+    hbm_frac = nbytes / sec / 1e9 / PEAK_HBM_GBS
+    if t_hbm >= t_mfma:
+        rec = {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 2), "peak": PEAK_HBM_GBS,
+               "unit": "GB/s", "frac": round(hbm_frac, 4)}
+    else:
+        rec = {"bound": "mfma", "achieved": round(flops / sec / 1e12, 2), "peak": peak_mfma,
+               "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
+    rec.update({"mfma_frac": round(mfma_frac, 4), "hbm_frac": round(hbm_frac, 4)})
+    return rec, flops, nbytes
+
+
+class Runner:
+    """Device copies of one workload's inputs and the step that runs on them."""
+
+    def __init__(self, wid, n_sets_arg, torch, bbsa, workloads):
+        self.w = w = workloads.WORKLOADS[wid]
+        elt = 2 if w.dtype == "bf16" else 4
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        log(f"workload {w.name}: generating inputs")
+        self.inp = workloads.make_inputs(wid)
+        self.plan = bbsa.bbsa_plan_rand_attn(w.H, w.nb, w.r, w.plan_seed)
+        dev = torch.device("cuda:0")
+        set_bytes = 4 * w.B * w.H * w.L * w.d * elt
+        # Enough copies that one pass over them moves three times the 256 MB
+        # last-level cache: no step reads inputs another step left in cache.
+        self.n_sets = n_sets_arg or max(1, int(np.ceil(768e6 / set_bytes)))
+        base = [torch.from_numpy(self.inp[n]).to(tdt).to(dev) for n in ("q", "k", "v")]
+        self.sets = []
+        for _ in range(self.n_sets):
+            q, k, v = (t.clone() for t in base)
+            self.sets.append((q, k, v, torch.empty_like(q)))
+        del base
+        self.mask = torch.from_numpy(self.inp["mask"]).to(dev)
+        self.ra = torch.from_numpy(self.plan).to(dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.bbsa = bbsa
+        self.torch = torch
+
+    def step(self, i):
+        q, k, v, o = self.sets[i % self.n_sets]
+        self.bbsa.bbsa_forward(q, k, v, self.mask, self.ra, self.w.block, self.w.r, out=o,
+                               stream=self.stream)
+
+    def preroll(self, seconds):
+        """Untimed steps for a fixed wall time before the warm-up steps: the
+        GPU's clocks need tens of milliseconds of sustained work to ramp up."""
+        torch = self.torch
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(50):
+                self.step(i)
+                i += 1
+            torch.cuda.synchronize()
+        return i
+
+    def timed(self, steps, warmup, same_set=False):
+        """Average step time in ms over ``steps`` back-to-back steps, bracketed
+        by events on the launch stream (after ``warmup`` untimed steps)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(0 if same_set else i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(steps):
+            self.step(0 if same_set else i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def percentiles(self, steps):
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(steps, 1000))]
+        for i, (a, b) in enumerate(ev):
+            a.record(self.stream)
+            self.step(i)
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return [round(float(np.percentile(per_step, x)), 2) for x in (10, 50, 90)]
+
+    def kernel_events(self, steps):
+        """The library's own events around each kernel: per-launch durations of
+        the attention kernel and of the merge kernel (0 when none runs)."""
+        bbsa, torch = self.bbsa, self.torch
+        bbsa.bbsa_timing_enable(True)
+        for i in range(min(steps, 4096)):
+            self.step(i)
+        torch.cuda.synchronize()
+        main_ms, comb_ms, calls = bbsa.bbsa_timing_read()
+        bbsa.bbsa_timing_enable(False)
+        return main_ms / max(calls, 1) * 1e3, comb_ms / max(calls, 1) * 1e3
+
+    def close(self):
+        self.sets = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    # The GPU's clocks take tens of milliseconds of sustained work to ramp up;
-    # the default warm-up (about 0.15 s of work at L=4096) covers that.
     ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--workload", type=int, default=2, help="headline workload id 1..5 (default 2)")
+    ap.add_argument("--others", default="3,4,5",
+                    help="other workload ids timed in the same run ('' for none)")
+    ap.add_argument("--preroll", type=float, default=0.3,
+                    help="seconds of untimed steps before each workload's warm-up (clock ramp)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,91 +284,52 @@ def main():
         print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
         return
 
-    w = workloads.WORKLOADS[args.workload]
-    elt = 2 if w.dtype == "bf16" else 4
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    log(f"workload {w.name}: generating inputs")
-    inp = workloads.make_inputs(args.workload)
-    plan = bbsa.bbsa_plan_rand_attn(w.H, w.nb, w.r, w.plan_seed)
-    dev = torch.device("cuda:0")
-    set_bytes = 4 * w.B * w.H * w.L * w.d * elt
-    n_sets = args.sets or max(1, int(np.ceil(768e6 / set_bytes)))
-    base = [torch.from_numpy(inp[n]).to(tdt).to(dev) for n in ("q", "k", "v")]
-    sets = []
-    for i in range(n_sets):
-        q, k, v = (t.clone() for t in base)
-        sets.append((q, k, v, torch.empty_like(q)))
-    mask = torch.from_numpy(inp["mask"]).to(dev)
-    ra = torch.from_numpy(plan).to(dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        q, k, v, o = sets[i % n_sets]
-        bbsa.bbsa_forward(q, k, v, mask, ra, w.block, w.r, out=o, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # Per-step distribution: each step bracketed by its own events.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(args.steps, 1000))]
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    p10, p50, p90 = (float(np.percentile(per_step, x)) for x in (10, 50, 90))
-
-    # Warm: the same input set every step (inputs can stay in the 256 MB cache).
-    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e2.record(stream)
-    for i in range(args.steps):
-        step(0)
-    e3.record(stream)
-    torch.cuda.synchronize()
-    warm_us = e2.elapsed_time(e3) / args.steps * 1e3
-
-    # Same steps again with the library's own HIP events around each kernel.
-    bbsa.bbsa_timing_enable(True)
-    for i in range(min(args.steps, 4096)):
-        step(i)
-    torch.cuda.synchronize()
-    main_ms, comb_ms, calls = bbsa.bbsa_timing_read()
-    bbsa.bbsa_timing_enable(False)
-    main_ms /= max(calls, 1)
-    comb_ms /= max(calls, 1)
-
-    flops = useful_flops(w.B, w.H, w.nb, w.block, w.d, w.r)
-    nbytes = algorithmic_bytes(w.B, w.H, w.L, w.d, w.nb, w.r, elt)
-    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    t_mfma = flops / (peak_mfma * 1e12)
-    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-    bound = "hbm" if t_hbm >= t_mfma else "mfma"
-    if bound == "hbm":
-        achieved = nbytes / (main_ms * 1e-3) / 1e9
-        peak, unit = PEAK_HBM_GBS, "GB/s"
-    else:
-        achieved = flops / (main_ms * 1e-3) / 1e12
-        peak, unit = peak_mfma, "TFLOP/s"
+    # Headline workload.
+    run = Runner(args.workload, args.sets, torch, bbsa, workloads)
+    w, n_sets = run.w, run.n_sets
+    pre = run.preroll(args.preroll)
+    ms = run.timed(args.steps, args.warmup)
+    p10, p50, p90 = run.percentiles(args.steps)
+    warm_us = run.timed(args.steps, 0, same_set=True) * 1e3
+    kern_us, merge_us = run.kernel_events(args.steps)
+    roof, flops, nbytes = roofline(w, ms)
+    roof["traffic"] = read_traffic(w.name)
+    roof["kernel"] = "bbsa_attn_bf16" if w.dtype == "bf16" else "bbsa_attn_f32"
+    # The step is one attention-kernel launch (plus the merge kernel only for
+    # rows longer than 4096 keys), so the average launch duration over the
+    # timed region is the step time; per-launch events (which add their own
+    # overhead) are reported beside it.
+    roof["kernel_us"] = round(ms * 1e3, 3)
+    roof["per_launch_event_us"] = {"attention": round(kern_us, 3), "merge": round(merge_us, 3)}
     value = flops / (ms * 1e-3) / 1e12
-    log(f"step {ms * 1e3:.2f} us (p10/p50/p90 of single steps {p10:.1f}/{p50:.1f}/{p90:.1f}, warm {warm_us:.1f}); "
-        f"main kernel {main_ms * 1e3:.2f} us, merge {comb_ms * 1e3:.2f} us; "
-        f"{value:.1f} useful TFLOP/s; MFMA util {flops / (main_ms * 1e-3) / 1e12 / peak_mfma:.3f}; "
-        f"HBM util {nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f}")
-
+    log(f"{w.name}: step {ms * 1e3:.2f} us (p10/p50/p90 {p10}/{p50}/{p90}, warm {warm_us:.1f}); "
+        f"{value:.1f} useful TFLOP/s; frac {roof['frac']} ({roof['bound']}); "
+        f"MFMA {roof['mfma_frac']} HBM {roof['hbm_frac']}")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
-        cpu = cpu_baseline(inp, plan, w, args.cpu_budget)
+        cpu = cpu_baseline(run.inp, run.plan, w, args.cpu_budget)
+    run.close()
+    del run
+
+    # Other workloads at L >= 4096, same protocol, one JSON entry each.
+    others = []
+    for tok in [t for t in args.others.split(",") if t.strip()]:
+        wid = int(tok)
+        if wid == args.workload:
+            continue
+        r2 = Runner(wid, args.sets, torch, bbsa, workloads)
+        r2.preroll(args.preroll)
+        ms2 = r2.timed(args.steps, args.warmup)
+        rf2, fl2, nb2 = roofline(r2.w, ms2)
+        v2 = fl2 / (ms2 * 1e-3) / 1e12
+        log(f"{r2.w.name}: step {ms2 * 1e3:.2f} us; {v2:.1f} useful TFLOP/s; frac {rf2['frac']} "
+            f"({rf2['bound']}); MFMA {rf2['mfma_frac']} HBM {rf2['hbm_frac']}")
+        others.append({"workload": r2.w.name, "step_us": round(ms2 * 1e3, 3),
+                       "useful_tflops": round(v2, 3), "useful_gflop_per_step": round(fl2 / 1e9, 3),
+                       "algorithmic_mb_per_step": round(nb2 / 1e6, 3), "roofline": rf2})
+        r2.close()
+        del r2
 
     rec = {
         "metric": METRIC,
@@ -244,15 +347,12 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "block": w.block,
                    "r": w.r, "useful_gflop_per_step": round(flops / 1e9, 3),
                    "algorithmic_mb_per_step": round(nbytes / 1e6, 3), "input_sets": n_sets,
-                   "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+                   "step_us_p10_p50_p90": [p10, p50, p90],
                    "warm_step_us": round(warm_us, 2),
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name),
-                     "kernel": "bbsa_attn_bf16" if w.dtype == "bf16" else "bbsa_attn_f32", "kernel_us": round(main_ms * 1e3, 3),
-                     "merge_kernel_us": round(comb_ms * 1e3, 3),
-                     "mfma_frac": round(flops / (main_ms * 1e-3) / 1e12 / peak_mfma, 4),
-                     "hbm_frac": round(nbytes / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                   "preroll": {"seconds": args.preroll, "steps": pre},
+                   "parallelism": "none (1 GPU)",
+                   "other_workloads": others},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -23,6 +23,9 @@ BBSA_ERR_SHAPE = -2
 BBSA_ERR_UNSUPPORTED = -3
 BBSA_ERR_HIP = -4
 BBSA_ERR_PLAN = -5
+BBSA_ERR_CAPTURE = -6
+
+WORK_RECORD_INTS = 80
 
 _LIB = None
 
@@ -53,6 +56,13 @@ def lib() -> ctypes.CDLL:
         L.bbsa_plan_rand_attn.restype = ctypes.c_int
         L.bbsa_check_rand_attn.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.bbsa_check_rand_attn.restype = ctypes.c_int
+        L.bbsa_plan_rand_attn_capped.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                                 ctypes.c_int, ctypes.c_int]
+        L.bbsa_plan_rand_attn_capped.restype = ctypes.c_int
+        L.bbsa_check_rand_attn_capped.argtypes = [i32p] + [ctypes.c_int] * 5
+        L.bbsa_check_rand_attn_capped.restype = ctypes.c_int
+        L.bbsa_truncate_rand_attn.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int]
+        L.bbsa_truncate_rand_attn.restype = ctypes.c_int
         L.bbsa_forward.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + \
             [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.bbsa_forward.restype = ctypes.c_int
@@ -67,6 +77,9 @@ def lib() -> ctypes.CDLL:
         dp = ctypes.POINTER(ctypes.c_double)
         L.bbsa_timing_read.argtypes = [dp, dp, ctypes.POINTER(ctypes.c_int)]
         L.bbsa_timing_read.restype = ctypes.c_int
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.bbsa_work_map.argtypes = [ctypes.c_int] * 7 + [i32p, i32p, ctypes.c_int64, i64p, i64p]
+        L.bbsa_work_map.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -97,6 +110,37 @@ def bbsa_check_rand_attn(rand_attn: np.ndarray, nb: int, r: int) -> int:
     if ra.ndim != 3 or ra.shape[1] != nb - 2 or ra.shape[2] != r:
         return BBSA_ERR_SHAPE
     return lib().bbsa_check_rand_attn(ra.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), H, int(nb), int(r))
+
+
+def bbsa_plan_rand_attn_capped(H: int, nb: int, r: int, seed: int, block: int, last_idx: int) -> np.ndarray:
+    """Host plan with the random range capped to the first ``last_idx``
+    tokens (see include/bbsa.h)."""
+    n = max(H, 0) * max(nb - 2, 0) * max(r, 0)
+    buf = np.zeros(max(n, 1), dtype=np.int32)
+    st = lib().bbsa_plan_rand_attn_capped(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(H), int(nb),
+                                          int(r), ctypes.c_uint64(int(seed) & (2**64 - 1)), int(block),
+                                          int(last_idx))
+    if st < 0:
+        raise BbsaError(st, "bbsa_plan_rand_attn_capped")
+    return buf[:n].reshape(H, nb - 2, r)
+
+
+def bbsa_check_rand_attn_capped(rand_attn: np.ndarray, nb: int, r: int, block: int, last_idx: int) -> int:
+    ra = np.ascontiguousarray(rand_attn, dtype=np.int32)
+    if ra.ndim != 3 or ra.shape[1] != nb - 2 or ra.shape[2] != r:
+        return BBSA_ERR_SHAPE
+    return lib().bbsa_check_rand_attn_capped(ra.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ra.shape[0],
+                                             int(nb), int(r), int(block), int(last_idx))
+
+
+def bbsa_truncate_rand_attn(rand_attn: np.ndarray, nb: int):
+    """Returns ``(status, plan)``: the first nb-2 rows of a longer plan."""
+    src = np.ascontiguousarray(rand_attn, dtype=np.int32)
+    H, rows, r = src.shape
+    dst = np.zeros((H, max(nb - 2, 1), r), dtype=np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    st = lib().bbsa_truncate_rand_attn(src.ctypes.data_as(i32p), H, rows + 2, r, dst.ctypes.data_as(i32p), int(nb))
+    return st, dst[:, :max(nb - 2, 0)]
 
 
 def _dtype_code(t):
@@ -154,7 +198,7 @@ def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=
                                 B, H, L, d, int(block), int(r), out.data_ptr(),
                                 ctypes.c_void_p(handle), code)
     if st < 0:
-        if st == BBSA_ERR_HIP:
+        if st in (BBSA_ERR_HIP, BBSA_ERR_CAPTURE):
             raise BbsaError(st, "bbsa_forward")
         raise ValueError(f"bbsa_forward: status {st}: {bbsa_status_string(st)}")
     if st == BBSA_OK_FULL_FALLBACK and warn_fallback:
@@ -179,3 +223,24 @@ def bbsa_timing_read():
     if st < 0:
         raise BbsaError(st, "bbsa_timing_read")
     return a.value, c.value, n.value
+
+
+def bbsa_work_map(B: int, H: int, L: int, d: int, block: int, r: int, dtype: int, rand_attn=None):
+    """The attention kernel's work decomposition for a call's shape (see
+    ``bbsa_work_map`` in include/bbsa.h): returns ``(status, grid, records)``
+    with ``records`` an int32 array ``[units, 80]``."""
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    ra = None
+    rptr = None
+    if rand_attn is not None:
+        ra = np.ascontiguousarray(rand_attn, dtype=np.int32)
+        rptr = ra.ctypes.data_as(i32p)
+    count, grid = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().bbsa_work_map(B, H, L, d, block, r, dtype, rptr, None, 0, ctypes.byref(count),
+                             ctypes.byref(grid))
+    if st < 0:
+        return st, 0, np.zeros((0, WORK_RECORD_INTS), dtype=np.int32)
+    rec = np.zeros((max(count.value, 1), WORK_RECORD_INTS), dtype=np.int32)
+    st = lib().bbsa_work_map(B, H, L, d, block, r, dtype, rptr, rec.ctypes.data_as(i32p), count.value,
+                             ctypes.byref(count), ctypes.byref(grid))
+    return st, grid.value, rec[:count.value]

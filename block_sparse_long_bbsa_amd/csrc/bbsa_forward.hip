@@ -33,18 +33,25 @@
 //     the fp32 path) leave partials in a workspace for a second kernel;
 //   * workgroups are mapped onto the 8 XCDs so that all items of one
 //     (batch, head) run on one XCD and share its L2.
+// The work decomposition itself (launch sizing, item mapping, key-block
+// lists) is in bbsa_schedule.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "bbsa.h"
+#include "bbsa_schedule.h"
 
 
 namespace {
+
+using namespace bbsa_sched;
 
 typedef __bf16 bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,117 +62,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kD = 64;        // head dimension
-constexpr int kQT = 64;       // query rows per wavefront
-constexpr int kStep = 32;     // keys per softmax step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPadBias = -10000.0f;
 // Lazy rescale threshold (raw score units): unnormalised probabilities stay <= 2^8.
 constexpr float kTau = 8.0f / 1.4426950408889634f;
 constexpr float kTauLog2 = 8.0f;
 constexpr float kInitMax = -1.0e30f;
-// One split-K partial: O[64][64] fp32, then the 64 reference maxima (log2
-// units), then the 64 row sums.
-constexpr int kPartialFloats = kQT * kD + 2 * kQT;
-
-// Division of 31-bit non-negative integers by a divisor fixed at launch:
-// q = (mulhi(n, m) + n) >> s with s = ceil(log2 d) and
-// m = floor(2^32 (2^s - d) / d) + 1 (the round-up method of Granlund and
-// Montgomery, "Division by invariant integers using multiplication", 1994).
-struct FastDiv {
-  uint32_t d, m, s;
-};
-inline FastDiv make_fastdiv(uint32_t d) {
-  FastDiv f;
-  f.d = d;
-  f.s = 0;
-  while ((1ull << f.s) < d) ++f.s;
-  f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
-  return f;
-}
-__device__ inline int fdiv(int n, const FastDiv &f) {
-  const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)n * f.m) >> 32);
-  return (int)((hi + (uint32_t)n) >> f.s);
-}
-
-struct Params {
-  const void *q, *k, *v;
-  const float *mask;         // [B, L] or null
-  const int32_t *rand_attn;  // [H, nb-2, r]
-  void *out;
-  float *ws;                 // split-K partials
-  int64_t seq_stride;        // L * d elements per (batch, head)
-  int B, H, L, nb, block, r;
-  int qtiles;                // block / 64
-  int n_rows_global;         // query blocks handled as full rows: 2, or nb on the fallback
-  int chunks;                // key chunks per full row (block range [c nb / chunks, (c + 1) nb / chunks))
-  int group;                 // items per workgroup: 4 on the bf16 path (a full row's chunks in fours), else 1
-  int nparts;                // split-K partials per full row left for the merge kernel: chunks / group
-  int mparts;                // key parts per middle row (fp32 path with few items: 2; else 1)
-  int comb_rows_global;      // per (batch, head): full rows the merge kernel combines (0 or n_rows_global)
-  int comb_rows_mid;         // per (batch, head): middle rows the merge kernel combines (0 or nb - 2)
-  int64_t mid_part_base;     // index of the first middle-row partial in the workspace
-  int n_global_items;        // per (batch, head): n_rows_global * qtiles * chunks
-  int items_per_bh;          // n_global_items + middle items
-  int bh_total;              // B * H
-  int xcd_remap;             // 1: map workgroups so one (batch, head) stays on one XCD
-  int n_glob;                // full-row items before the first middle item (per XCD lane)
-  FastDiv div_global;        // n_global_items
-  FastDiv div_mid;           // middle items per (batch, head), at least 1
-  FastDiv div_row;           // qtiles * chunks
-  FastDiv div_chunks;        // chunks
-  FastDiv div_qtiles;        // qtiles
-  FastDiv div_mparts;        // mparts
-  FastDiv div_heads;         // H
-};
-
-// A work item: 64 query rows (query tile qt of query block qblock) of one
-// (batch, head), against either the middle row's key blocks or one chunk of
-// a full row.
-struct Item {
-  int bh;
-  int qblock;
-  int qt;
-  int grow;       // full-row index (partials), -1 for a middle row
-  int chunk;      // key chunk of a full row, or key part of a middle row
-};
-
-// Workgroup -> item.  Workgroups are dispatched in index order, so the
-// longest items (full-row chunks) of every (batch, head) come first and the
-// middle rows fill in behind them; this keeps long items out of the tail.
-// With the XCD remap, workgroup w runs on XCD x = w % 8 and serves only the
-// (batch, head) pairs x, x + 8, x + 16, ..., so all items of one pair share
-// one L2.
-// With p.group items per workgroup, wavefront wv of workgroup wg takes item
-// wv of the workgroup's run of p.group consecutive items; the full-row items
-// of a pair come as whole groups (their count is a multiple of p.group), so
-// a group of full-row items is the p.group chunks of one row tile.
-// All divisions use the launch's precomputed FastDiv constants.
-__device__ inline Item decode_item(const Params &p, int wg, int wv) {
-  const int lg_lanes = p.xcd_remap ? 3 : 0;
-  const int x = wg & ((1 << lg_lanes) - 1), slot = (wg >> lg_lanes) * p.group + wv;
-  const bool g = slot < p.n_glob;
-  const int sg = g ? slot : 0, sm = g ? 0 : slot - p.n_glob;
-  const int jg = fdiv(sg, p.div_global), jm = fdiv(sm, p.div_mid);
-  const int j = g ? jg : jm;
-  const int local = g ? sg - jg * p.n_global_items : p.n_global_items + (sm - jm * (int)p.div_mid.d);
-  const int bh = x + (j << lg_lanes);
-  const bool global_row = local < p.n_global_items;
-  const int lr = global_row ? local : 0;
-  const int m = global_row ? 0 : local - p.n_global_items;
-  const int grow = fdiv(lr, p.div_row);
-  const int rem = lr - grow * (int)p.div_row.d;
-  const int qt_g = fdiv(rem, p.div_chunks);
-  const int mp = fdiv(m, p.div_mparts);   // middle item m = key part + mparts * (query tile + qtiles * row)
-  const int mq = fdiv(mp, p.div_qtiles);
-  Item it;
-  it.bh = bh;   // >= bh_total marks an idle workgroup
-  it.grow = global_row ? grow : -1;
-  it.qt = global_row ? qt_g : mp - mq * p.qtiles;
-  it.chunk = global_row ? rem - qt_g * p.chunks : m - mp * p.mparts;
-  it.qblock = global_row ? ((p.n_rows_global == 2) ? (grow == 0 ? 0 : p.nb - 1) : grow) : 1 + mq;
-  return it;
-}
 
 __device__ inline float group4_max(float x) {
   // Lanes l, l^16, l^32, l^48 hold the same query column.
@@ -183,18 +85,19 @@ __device__ inline float group4_sum(float x) {
 
 // fp32 path: each wavefront owns kNT 16-query tiles of its item.
 constexpr int kNT = 1;
-constexpr int kF32Waves = 4 / kNT;   // wavefronts per fp32 workgroup (one item)
-// Below this many wavefronts (about two per SIMD) the fp32 path cuts its work
-// finer: full-row chunks of kF32SmallChunkKeys keys, middle rows in
-// kF32SmallParts key parts.
-constexpr int64_t kF32SplitBelowWaves = 2048;
-constexpr int kF32SmallChunkKeys = 128;
-constexpr int kF32SmallParts = 4;
+static_assert(kF32Waves * kNT == 4, "the fp32 workgroup's wavefronts split an item's four 16-row tiles");
 
 // Online-softmax state of the kNT query columns a lane holds (one per 16-query tile nt).
+// The scores are taken relative to a padding-bias level: key k contributes
+// s_k + (bias_k - level), where level is the largest bias among the keys seen
+// so far (uniform over the wavefront).  A row whose keys all share one mask
+// value therefore sees its scores unchanged, instead of s_k - 10000 rounded
+// to fp32's spacing of about 1e-3 at that magnitude; keys below the level
+// carry the (exact, for 0/1 masks) difference.
 struct SoftmaxState {
-  float m[kNT];   // reference max (raw score units), identical across the 4 lane groups
+  float m[kNT];   // reference max (raw score units, relative to the level), identical across the 4 lane groups
   float l[kNT];   // per-lane partial row sum of exp2 values
+  float level;    // padding-bias level (uniform)
 };
 
 // Lazy rescale for one 32-key step.  s[mt][nt][i] holds the score of key
@@ -254,15 +157,34 @@ __device__ inline void row_sum_f32(const f32x4 (&s)[2][kNT], SoftmaxState &st) {
   }
 }
 
-// Add the key-side padding bias to every score when any key of this step is padded.
-__device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2]) {
+// Add the key-side padding bias, relative to the state's level, to every
+// score.  A step whose largest bias exceeds the level raises the level first;
+// the reference max moves down by the same amount, so it stays the same
+// absolute value (what was accumulated against the old level is rescaled, or
+// vanishes, through the ordinary rescale that follows).
+__device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2], SoftmaxState &st) {
   float bias[2][4];
-  bool any = false;
+  float bmax = kInitMax;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bias[mt][i] = kPadBias * (1.0f - mk[mt][i]);
+      bmax = __builtin_fmaxf(bmax, bias[mt][i]);
+    }
+  // Lanes l, l^16, l^32, l^48 hold the step's four groups of 8 keys.
+  bmax = group4_max(bmax);
+  if (bmax > st.level) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) st.m[nt] += st.level - bmax;
+    st.level = bmax;
+  }
+  bool any = false;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bias[mt][i] -= st.level;
       any |= bias[mt][i] != 0.0f;
     }
   if (__builtin_amdgcn_ballot_w64(any)) {
@@ -274,16 +196,6 @@ __device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2]) {
         for (int i = 0; i < 4; ++i) s[mt][nt][i] += bias[mt][i];
   }
 }
-
-// The key blocks an item walks, one 32-key step at a time.  At item start,
-// lane t of `blk` holds the t-th key block of the item (at most 64 blocks);
-// steps read it back with v_readlane, so advancing touches no memory.
-struct KeyWalk {
-  int n_steps;
-  int steps_per_block;
-  int blk;             // per lane: key block at list position `lane`
-  int first_blk;       // the block at position 0 (uniform)
-};
 
 struct WalkCursor {
   int t, sb, key0;
@@ -309,53 +221,13 @@ struct WalkCursor {
   }
 };
 
-// The key block list of an item, in two parts so that the plan entries can
-// be loaded early and used late: make_walk_base fills everything but the
-// random blocks and starts the load of the lane's plan entry (rnd; rslot is
-// the lane's slot in the plan row, -1 if none); merge_plan puts the random
-// blocks in (clamped so that a bad plan never reads outside the sequence).
 __device__ inline int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() & 63; }
 
-__device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int &rnd, int &rslot) {
-  const int lane = lane_id();
-  KeyWalk w;
-  w.steps_per_block = p.block / kStep;
-  // Uniform quantities first (kept in scalar registers), then the per-lane list.
-  const bool middle = it.grow < 0;
-  const int i = it.qblock;
-  const int nw = (i == 1 || i == p.nb - 2) ? 2 : 3;
-  const int first = fdiv(it.chunk * p.nb, p.div_chunks);
-  const int nblk = middle ? 2 + nw + p.r : fdiv((it.chunk + 1) * p.nb, p.div_chunks) - first;   // may be 0 if nb < chunks
-  w.n_steps = __builtin_amdgcn_readfirstlane(nblk * w.steps_per_block);
-  w.first_blk = middle ? 0 : first;
-  int blk;
-  rslot = -1;
-  rnd = 0;
-  if (middle) {
-    // Middle query block i: the two global blocks, the window without them,
-    // then the random blocks.
-    const int w0 = (i == 1) ? 1 : i - 1;
-    const int h = it.bh - fdiv(it.bh, p.div_heads) * p.H;
-    const int32_t *ra_row = p.rand_attn + ((int64_t)h * (p.nb - 2) + (i - 1)) * p.r;
-    const int t = lane - 2 - nw;
-    rnd = ra_row[min(max(t, 0), p.r - 1)];
-    rslot = (t >= 0 && t < p.r) ? t : -1;
-    blk = 0;
-    if (lane == 1) blk = p.nb - 1;
-    else if (lane >= 2 && lane < 2 + nw) blk = w0 + (lane - 2);
-  } else {
-    blk = first + max(min(lane, nblk - 1), 0);
-  }
-  w.blk = blk;
-  return w;
-}
-__device__ inline void merge_plan(const Params &p, KeyWalk &w, int rnd, int rslot) {
-  if (rslot >= 0) w.blk = min(max(rnd, 0), p.nb - 1);
-}
 __device__ inline KeyWalk make_walk(const Params &p, const Item &it) {
   int rnd, rslot;
-  KeyWalk w = make_walk_base(p, it, rnd, rslot);
+  KeyWalk w = make_walk_base(p, it, lane_id(), rnd, rslot);
   merge_plan(p, w, rnd, rslot);
+  w.n_steps = __builtin_amdgcn_readfirstlane(w.n_steps);
   return w;
 }
 
@@ -389,10 +261,12 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, int 
     if (g == 0) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        part[kQT * kD + 16 * (nt0 + nt) + c] = st.m[nt] * kLog2e;   // log2 units
+        part[kQT * kD + 16 * (nt0 + nt) + c] = st.m[nt] * kLog2e;   // log2 units, relative to the level
         part[kQT * kD + kQT + 16 * (nt0 + nt) + c] = lsum[nt];
       }
     }
+    // Every wavefront of the item holds the same level; the first one stores it.
+    if (lane == 0 && nt0 == 0) part[kQT * kD + 2 * kQT] = st.level;
     return;
   }
   OutT *out = (OutT *)p.out + (int64_t)it.bh * p.seq_stride;
@@ -458,7 +332,6 @@ __device__ inline float swap_halves(float x) {
   return __uint_as_float(lane < 32 ? a[1] : a[0]);
 }
 
-constexpr int kGroup = 4;                        // wavefronts (items) per bf16 workgroup
 constexpr int kWaveLds = 4 * kTileBytes;          // 16 KB per wavefront: K and V double buffers
 
 // One wavefront per item, kGroup items per workgroup.  The wavefronts of a
@@ -527,8 +400,8 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
   // The plan entries are merged into the walk after the prologue's wait: the
   // first two K tiles lie in the first block and do not need them.
   int rnd, rslot;
-  KeyWalk walk = make_walk_base(p, it, rnd, rslot);
-  const int n = walk.n_steps;                 // >= 2
+  KeyWalk walk = make_walk_base(p, it, lane, rnd, rslot);
+  const int n = __builtin_amdgcn_readfirstlane(walk.n_steps);   // >= 2, or 0 for an empty chunk
   // First key of step i: block i / steps_per_block of the list (a lane of
   // walk.blk), then 32 keys per step inside it.  Branch-free; uniform.
   const int lg_spb = walk.steps_per_block >> 1;      // steps_per_block is 2 or 4
@@ -839,7 +712,8 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
       __builtin_nontemporal_store(v0, (bf16x8 *)orow);
       __builtin_nontemporal_store(v1, (bf16x8 *)(orow + 8));
     } else {
-      // A partial over this group of chunks for the merge kernel.
+      // A partial over this group of chunks for the merge kernel (bias
+      // level 0: the bf16 scores carry the whole padding bias).
       const int64_t pidx = (((int64_t)it.bh * p.n_rows_global + it.grow) * p.qtiles + it.qt) * p.nparts + it.chunk / kGroup;
       float *part = p.ws + pidx * kPartialFloats;
 #pragma unroll
@@ -848,6 +722,7 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
         part[kQT * kD + r] = M;
         part[kQT * kD + kQT + r] = den;
       }
+      if (wv == 0 && lane == 0) part[kQT * kD + 2 * kQT] = 0.0f;
     }
     return;
   }
@@ -919,6 +794,7 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
   SoftmaxState st;
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) { st.m[nt] = kInitMax; st.l[nt] = 0.0f; }
+  st.level = HAS_MASK ? kInitMax : 0.0f;
   f32x4 o[4][kNT];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -986,7 +862,7 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
       }
     if (HAS_MASK) {
       f32x4 mc[2] = {x.mc[0], x.mc[1]};
-      apply_mask(s, mc);
+      apply_mask(s, mc, st);
     }
     softmax_rescale(s, st, o);
     softmax_exp(s, st);
@@ -1010,7 +886,6 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
 // slice); 16 threads per query, each owning 4 consecutive d:
 // out = sum_c w_c O_c / sum_c w_c l_c with w_c = 2^(m_c - M), M the largest
 // reference maximum (log2 units), accumulated in one pass.
-constexpr int kMergeSlices = kQT / 4;
 constexpr int kMergeBatch = 8;   // chunks whose loads are in flight together
 template <typename OutT>
 __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
@@ -1030,6 +905,11 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const float *base = p.ws + first * kPartialFloats;
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int q = 4 * slice + (tid >> 4), dq = tid & 15;
+  // Each partial's maxima are relative to its padding-bias level: partial c
+  // enters with exponent m_c + (level_c - top level) * log2(e), where the
+  // level difference is exact for 0/1 masks (and 0 on the bf16 path).
+  float top = kInitMax;
+  for (int ch = 0; ch < np; ++ch) top = __builtin_fmaxf(top, base[(int64_t)ch * kPartialFloats + kQT * kD + 2 * kQT]);
   // One pass, kMergeBatch chunks at a time: all loads of a batch are issued
   // before any of them is used; the running (M, den, acc) is rescaled when a
   // batch raises the maximum.
@@ -1042,7 +922,7 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
     for (int u = 0; u < kMergeBatch; ++u) {
       const int ch = min(c0 + u, np - 1);   // repeats stay unused
       const float *part = base + (int64_t)ch * kPartialFloats;
-      mc[u] = part[kQT * kD + q];
+      mc[u] = part[kQT * kD + q] + (part[kQT * kD + 2 * kQT] - top) * kLog2e;
       lc[u] = part[kQT * kD + kQT + q];
       oc[u] = *(const f32x4 *)(part + q * kD + 4 * dq);
     }
@@ -1073,16 +953,23 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
 
 // ---------------------------------------------------------------- host side
 
+// Library-owned split-K workspaces, one per (device, stream): calls on one
+// stream are ordered by the stream, calls on different streams never share
+// a buffer.  A workspace grows in powers of two; the buffer it outgrows is
+// kept (not freed) until bbsa_release_workspace, because kernels already
+// enqueued, or a HIP graph captured earlier, may still use it.
 struct DeviceWorkspace {
-  void *ptr = nullptr;       // split-K partials
+  void *ptr = nullptr;
   size_t bytes = 0;
 };
 
-std::mutex g_mutex;
-std::vector<DeviceWorkspace> g_ws;
+std::mutex g_mutex;                                          // guards g_ws, g_retired
+std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_ws;
+std::vector<std::pair<int, void *>> g_retired;               // (device, buffer)
 
 constexpr int kMaxTimed = 4096;
 struct Timing {
+  std::mutex mu;                                             // guards everything below
   bool enabled = false;
   bool created = false;
   int n = 0;
@@ -1091,22 +978,24 @@ struct Timing {
 };
 Timing g_timing;
 
-// Library-owned split-K workspace of the current device, grown on demand.
-int ensure_workspace(size_t bytes, float **ws) {
+int ensure_workspace(size_t bytes, hipStream_t stream, float **ws) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return BBSA_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_mutex);
-  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  DeviceWorkspace &w = g_ws[dev];
+  DeviceWorkspace &w = g_ws[std::make_pair(dev, stream)];
   if (w.bytes < bytes) {
-    if (w.ptr) {
-      if (hipDeviceSynchronize() != hipSuccess) return BBSA_ERR_HIP;
-      if (hipFree(w.ptr) != hipSuccess) return BBSA_ERR_HIP;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    if (hipMalloc(&w.ptr, bytes) != hipSuccess) { w.ptr = nullptr; return BBSA_ERR_HIP; }
-    w.bytes = bytes;
+    // Allocating is not allowed while the stream is being captured into a
+    // graph: the caller runs one eager call of the shape first.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return BBSA_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return BBSA_ERR_CAPTURE;
+    size_t grow = (size_t)1 << 20;
+    while (grow < bytes) grow <<= 1;
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, grow) != hipSuccess) return BBSA_ERR_HIP;
+    if (w.ptr) g_retired.emplace_back(dev, w.ptr);
+    w.ptr = ptr;
+    w.bytes = grow;
   }
   *ws = (float *)w.ptr;
   return BBSA_OK;
@@ -1116,94 +1005,27 @@ int ensure_workspace(size_t bytes, float **ws) {
 
 extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
                             const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
-                            void *out, hipStream_t stream, int dtype) {
-  if (!q || !k || !v || !out) return BBSA_ERR_ARG;
-  // The kernels move q, k, v, out and the mask in 16-byte pieces.
-  auto misaligned = [](const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) != 0; };
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
-      (mask && misaligned(mask, 16)) || (rand_attn && misaligned(rand_attn, 4)))
-    return BBSA_ERR_ARG;
-  if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block <= 0 || r < 1) return BBSA_ERR_ARG;
-  if (dtype != BBSA_BF16 && dtype != BBSA_F32) return BBSA_ERR_UNSUPPORTED;
-  if (d != kD || (block != 64 && block != 128)) return BBSA_ERR_UNSUPPORTED;
-  if (L % block != 0) return BBSA_ERR_SHAPE;
-  const int nb = L / block;
-  const bool full = (int64_t)L <= (int64_t)(5 + 2 * (int64_t)r) * block;
-  if (!full) {
-    if (!rand_attn) return BBSA_ERR_ARG;
-    if (nb < 5 + r) return BBSA_ERR_SHAPE;
-    if (5 + r > 64) return BBSA_ERR_UNSUPPORTED;   // a middle row lists at most 64 key blocks
-  }
-
-  Params p;
-  std::memset(&p, 0, sizeof(p));
-  p.q = q; p.k = k; p.v = v; p.mask = mask; p.rand_attn = rand_attn; p.out = out;
-  p.seq_stride = (int64_t)L * kD;
-  p.B = B; p.H = H; p.L = L; p.nb = nb; p.block = block; p.r = r;
-  p.qtiles = block / kQT;
-  p.n_rows_global = full ? nb : 2;
-  // Full rows are cut into chunks of about 1024 keys (bf16) or 256 keys (the
-  // slower fp32 path) so they do not form the tail.  On the bf16 path the
-  // chunk count is a multiple of kGroup: each workgroup runs kGroup chunks
-  // of one row tile and merges them in LDS, and the merge kernel combines
-  // the chunks / kGroup group results (none for rows of up to 4096 keys).
-  const int64_t bh = (int64_t)B * H;
-  int per_chunk = (dtype == BBSA_F32 ? 256 : 1024) / block;   // blocks
-  // The fp32 path has too few wavefronts for the chip when a call is small:
-  // then it cuts full rows into shorter chunks and middle rows into key parts
-  // (kF32SmallParts), all merged by the merge kernel.
-  bool f32_small = false;
-  if (dtype == BBSA_F32 && !full) {
-    const int64_t items = bh * p.qtiles * (2 * (int64_t)((nb + per_chunk - 1) / per_chunk) + (nb - 2));
-    if (items * kF32Waves < kF32SplitBelowWaves) {
-      f32_small = true;
-      per_chunk = std::max(1, kF32SmallChunkKeys / block);
-    }
-  }
-  if (dtype == BBSA_BF16) {
-    p.group = kGroup;
-    p.chunks = kGroup * ((nb + kGroup * per_chunk - 1) / (kGroup * per_chunk));
-  } else {
-    p.group = 1;
-    p.chunks = (nb + per_chunk - 1) / per_chunk;
-  }
-  p.nparts = p.chunks / p.group;
-  p.n_global_items = p.n_rows_global * p.qtiles * p.chunks;
-  p.mparts = f32_small ? kF32SmallParts : 1;
-  const int n_middle = full ? 0 : (nb - 2) * p.qtiles * p.mparts;
-  const int64_t items_per_bh = (int64_t)p.n_global_items + n_middle;
-  p.xcd_remap = bh >= 8 ? 1 : 0;
-  const int64_t items_per_lane = (p.xcd_remap ? (bh + 7) / 8 : bh) * items_per_bh;
-  const int64_t grid = (p.xcd_remap ? 8 : 1) * ((items_per_lane + p.group - 1) / p.group);
-  const int64_t n_part_full = (p.nparts > 1) ? bh * p.n_rows_global * p.qtiles * p.nparts : 0;
-  const int64_t n_part_mid = (p.mparts > 1) ? bh * (nb - 2) * p.qtiles * p.mparts : 0;
-  const int64_t n_partials = n_part_full + n_part_mid;
-  p.mid_part_base = n_part_full;
-  p.comb_rows_global = (p.nparts > 1) ? p.n_rows_global : 0;
-  p.comb_rows_mid = (p.mparts > 1) ? nb - 2 : 0;
-  const int64_t comb_grid = (int64_t)kMergeSlices * bh * (p.comb_rows_global + p.comb_rows_mid) * p.qtiles;
-  if (items_per_lane > 0x7fffffff || grid > 0x7fffffff || bh > 0x7fffffff || (int64_t)B * H * L * kD > ((int64_t)1 << 40) ||
-      comb_grid > 0x7fffffff)
-    return BBSA_ERR_UNSUPPORTED;
-  p.items_per_bh = (int)items_per_bh;
-  p.bh_total = (int)bh;
-  p.n_glob = (int)((p.xcd_remap ? (bh + 7) / 8 : bh) * p.n_global_items);
-  p.div_global = make_fastdiv((uint32_t)p.n_global_items);
-  p.div_mid = make_fastdiv((uint32_t)std::max(n_middle, 1));
-  p.div_row = make_fastdiv((uint32_t)(p.qtiles * p.chunks));
-  p.div_chunks = make_fastdiv((uint32_t)p.chunks);
-  p.div_qtiles = make_fastdiv((uint32_t)p.qtiles);
-  p.div_mparts = make_fastdiv((uint32_t)p.mparts);
-  p.div_heads = make_fastdiv((uint32_t)H);
-  if (n_partials > 0) {
-    const int rc = ensure_workspace((size_t)n_partials * kPartialFloats * sizeof(float), &p.ws);
+                            void *out, hipStream_t stream, bbsa_dtype dtype) {
+  Launch ln;
+  const int st = setup_forward(q, k, v, mask, rand_attn, B, H, L, d, block, r, out, (int)dtype, &ln);
+  if (st < 0) return st;
+  Params &p = ln.p;
+  if (ln.n_partials > 0) {
+    const int rc = ensure_workspace((size_t)ln.n_partials * kPartialFloats * sizeof(float), stream, &p.ws);
     if (rc != BBSA_OK) return rc;
   }
 
+  std::unique_lock<std::mutex> tlock(g_timing.mu);
   const bool timed = g_timing.enabled && g_timing.n < kMaxTimed;
   const int tslot = g_timing.n;
+  if (timed) {
+    g_timing.n++;
+    g_timing.has_combine[tslot] = ln.comb_grid > 0;
+  } else {
+    tlock.unlock();
+  }
   if (timed && hipEventRecord(g_timing.ev[tslot][0], stream) != hipSuccess) return BBSA_ERR_HIP;
-  const dim3 g1((unsigned)grid), b1(dtype == BBSA_BF16 ? 64 * p.group : 64 * kF32Waves);
+  const dim3 g1((unsigned)ln.grid), b1((unsigned)ln.block_threads);
   if (dtype == BBSA_BF16) {
     if (mask) hipLaunchKernelGGL(bbsa_attn_bf16<true>, g1, b1, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_attn_bf16<false>, g1, b1, 0, stream, p);
@@ -1213,19 +1035,15 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
   }
   if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
   if (timed && hipEventRecord(g_timing.ev[tslot][1], stream) != hipSuccess) return BBSA_ERR_HIP;
-  if (n_partials > 0) {
+  if (ln.comb_grid > 0) {
     if (timed && hipEventRecord(g_timing.ev[tslot][2], stream) != hipSuccess) return BBSA_ERR_HIP;
-    const dim3 g2((unsigned)comb_grid), b2(64);
+    const dim3 g2((unsigned)ln.comb_grid), b2(64);
     if (dtype == BBSA_BF16) hipLaunchKernelGGL(bbsa_combine<bf16_t>, g2, b2, 0, stream, p);
     else hipLaunchKernelGGL(bbsa_combine<float>, g2, b2, 0, stream, p);
     if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
     if (timed && hipEventRecord(g_timing.ev[tslot][3], stream) != hipSuccess) return BBSA_ERR_HIP;
   }
-  if (timed) {
-    g_timing.has_combine[tslot] = n_partials > 0;
-    g_timing.n++;
-  }
-  return full ? BBSA_OK_FULL_FALLBACK : BBSA_OK;
+  return st;
 }
 
 extern "C" const char *bbsa_status_string(int status) {
@@ -1237,6 +1055,7 @@ extern "C" const char *bbsa_status_string(int status) {
     case BBSA_ERR_UNSUPPORTED: return "unsupported configuration (d != 64, block not 64/128, dtype, or size)";
     case BBSA_ERR_HIP: return "HIP runtime error";
     case BBSA_ERR_PLAN: return "rand_attn violates the plan invariants";
+    case BBSA_ERR_CAPTURE: return "the workspace must grow while the stream is being captured (run one eager call of this shape first)";
     default: return "unknown status";
   }
 }
@@ -1245,21 +1064,27 @@ extern "C" void bbsa_release_workspace(void) {
   std::lock_guard<std::mutex> lock(g_mutex);
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return;
-  for (size_t dev = 0; dev < g_ws.size(); ++dev) {
-    DeviceWorkspace &w = g_ws[dev];
-    if (!w.ptr) continue;
-    if (hipSetDevice((int)dev) == hipSuccess) {
+  std::vector<std::pair<int, void *>> all = g_retired;
+  for (auto &kv : g_ws)
+    if (kv.second.ptr) all.emplace_back(kv.first.first, kv.second.ptr);
+  int synced = -1;
+  for (auto &dv : all) {
+    if (hipSetDevice(dv.first) != hipSuccess) continue;
+    if (synced != dv.first) {
       (void)hipDeviceSynchronize();
-      (void)hipFree(w.ptr);
+      synced = dv.first;
     }
-    w = DeviceWorkspace();
+    (void)hipFree(dv.second);
   }
+  g_ws.clear();
+  g_retired.clear();
   (void)hipSetDevice(cur);
 }
 
-extern "C" int bbsa_version(void) { return 100; }
+extern "C" int bbsa_version(void) { return 200; }
 
 extern "C" int bbsa_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   if (enable && !g_timing.created) {
     for (int i = 0; i < kMaxTimed; ++i)
       for (int j = 0; j < 4; ++j)
@@ -1273,6 +1098,7 @@ extern "C" int bbsa_timing_enable(int enable) {
 
 extern "C" int bbsa_timing_read(double *main_ms, double *combine_ms, int *calls) {
   if (!main_ms || !combine_ms || !calls) return BBSA_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   double a = 0.0, c = 0.0;
   for (int i = 0; i < g_timing.n; ++i) {
     float ms = 0.f;

@@ -2,26 +2,9 @@
  * bbsa.h -- C ABI of the BigBird block-sparse attention forward for AMD
  * Instinct MI355X (gfx950).
  *
- * The operation (pages cited by title and section):
- *
- *   "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践",
- *   section "BigBird：从二次方注意力到线性稀疏注意力": Q, K and V are split
- *   into blocks of `block` tokens; the first and the last query block attend
- *   to the whole sequence; every middle query block attends to the first and
- *   the last key block, to a 3-block window around itself and to
- *   `num_rand_blocks` (here `r`) random key blocks; masked positions get an
- *   additive -10000 before the row softmax.
- *
- *   Same page, section "随机块掩码是如何生成的": the random blocks of each
- *   middle row come from a per-head adjacency (`rand_attn`) that never
- *   overlaps the row's window; the plan is fixed per head when the layer is
- *   built, with the layer index as the seed.
- *
- *   "BigBirdPegasus 长序列条件生成模型详解从稀疏注意力原理到 Transformers 实战",
- *   sections "序列长度的块对齐要求" (length must be a multiple of the block:
- *   error otherwise), "序列过短时的自动回退" (full attention when the length
- *   does not exceed (5 + 2r) * block), "使用限制与注意事项" (r = 0 is not
- *   supported).
+ * The pages this library implements are cited by title and section:
+ *   [BB] "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践"
+ *   [BP] "BigBirdPegasus 长序列条件生成模型详解从稀疏注意力原理到 Transformers 实战"
  *
  * Readings taken where the pages are silent: no internal softmax scale (fold
  * 1/sqrt(d) into Q); the padding mask is applied on the key side only, as
@@ -34,11 +17,7 @@
  * block i.  Supported: d = 64, block in {64, 128}, bf16 or fp32 elements.
  *
  * Ownership: the caller owns every buffer it passes; the library never frees
- * caller memory.  The library owns one split-K workspace per device (grown on
- * demand with hipMalloc, released by bbsa_release_workspace); it is used only
- * when a row needs more than one partial: bf16 rows longer than 4096 keys,
- * fp32 rows longer than 256 keys, and, in fp32 calls with fewer than 2048
- * wavefronts of work, full rows longer than 128 keys and every middle row.
+ * caller memory.  The library owns split-K workspaces (see bbsa_forward).
  *
  * Errors: every function returns a status code (below); no C++ exception
  * crosses this interface.  Argument checks run on the host before any HIP
@@ -65,11 +44,20 @@ enum {
   BBSA_ERR_SHAPE = -2,       /* L % block != 0, or nb < 5 + r where a plan is required */
   BBSA_ERR_UNSUPPORTED = -3, /* d != 64, block not in {64, 128}, unknown dtype, too large */
   BBSA_ERR_HIP = -4,         /* a HIP call or kernel launch failed */
-  BBSA_ERR_PLAN = -5         /* rand_attn violates an invariant (bbsa_check_rand_attn) */
+  BBSA_ERR_PLAN = -5,        /* rand_attn violates an invariant (bbsa_check_rand_attn) */
+  BBSA_ERR_CAPTURE = -6      /* the workspace would have to grow during stream capture */
 };
 
 /*
  * Build the random-block adjacency on the host.
+ *
+ * Implements [BB] section "随机块掩码是如何生成的": every middle query block
+ * (all blocks but the first and the last) gets r random key blocks drawn from
+ * the middle blocks with its own 3-block window removed, fixed per head when
+ * the layer is built and seeded by the layer index; [BP] section
+ * "三类注意力组合全局 局部 随机" (num_random_blocks per query block).  The
+ * pages draw with numpy's permutation; this planner draws from a specified
+ * stream so that every implementation can reproduce the plan bit for bit.
  *
  * rand_attn: host buffer of H * (nb-2) * r int32, caller-owned, written as
  *            [H][nb-2][r].
@@ -87,15 +75,64 @@ enum {
 int bbsa_plan_rand_attn(int32_t *rand_attn, int H, int nb, int r, uint64_t seed);
 
 /*
- * Check a host plan [H][nb-2][r]: every entry a middle block (1..nb-2), the r
- * entries of a row distinct, none within distance 1 of the row's block.
- * Returns BBSA_OK, BBSA_ERR_PLAN on a violation, BBSA_ERR_ARG / _SHAPE on bad
- * arguments.
+ * Check a host plan [H][nb-2][r] against the invariants [BB] section
+ * "随机块掩码是如何生成的" fixes: every entry a middle block (1..nb-2), the r
+ * entries of a row distinct, none within distance 1 of the row's block (the
+ * random blocks never overlap the window).
+ *
+ * rand_attn: host buffer, read only.  Returns BBSA_OK, BBSA_ERR_PLAN on a
+ * violation, BBSA_ERR_ARG for a null buffer or H, nb, r < 1, BBSA_ERR_SHAPE
+ * when nb < 5 + r.
  */
 int bbsa_check_rand_attn(const int32_t *rand_attn, int H, int nb, int r);
 
 /*
+ * The plan with the random range capped, and its checker.
+ *
+ * Implements the limit [BB] section "随机块掩码是如何生成的" describes: the
+ * layer draws its random blocks only from the first last_idx = 1024 tokens,
+ * builds the plan once for its maximum length and uses its first
+ * from_seq_length / block - 2 rows for a shorter sequence.  With
+ * last_idx > 0, the candidates of every row are the blocks of
+ * bbsa_plan_rand_attn's list that lie wholly inside the first last_idx tokens
+ * (block c with (c + 1) * block <= last_idx); the stream, the shuffle and the
+ * layout are those of bbsa_plan_rand_attn, so a cap at or beyond block nb - 2
+ * gives exactly the uncapped plan.  last_idx <= 0 means no cap.
+ *
+ * rand_attn: host buffer [H][nb-2][r], caller-owned (written by the planner,
+ * read by the checker).  Returns BBSA_OK; BBSA_ERR_ARG for a null buffer,
+ * H, nb or r < 1, or last_idx > 0 with block < 1; BBSA_ERR_SHAPE when
+ * nb < 5 + r or the cap leaves some row fewer than r candidates;
+ * BBSA_ERR_PLAN (checker) when an entry breaks an invariant or the cap.
+ */
+int bbsa_plan_rand_attn_capped(int32_t *rand_attn, int H, int nb, int r, uint64_t seed,
+                               int block, int last_idx);
+int bbsa_check_rand_attn_capped(const int32_t *rand_attn, int H, int nb, int r, int block,
+                                int last_idx);
+
+/*
+ * Keep the first nb-2 rows of a plan built for nb_src >= nb blocks (the
+ * shorter-sequence use [BB] section "随机块掩码是如何生成的" describes).
+ * src: host [H][nb_src-2][r]; dst: host [H][nb-2][r], caller-owned.  Returns
+ * BBSA_OK when dst is a valid plan for nb blocks, BBSA_ERR_PLAN when a kept
+ * pick is not a middle block of the shorter sequence (or breaks another
+ * invariant), BBSA_ERR_ARG for null buffers, H or r < 1, nb < 3 or
+ * nb_src < nb.
+ */
+int bbsa_truncate_rand_attn(const int32_t *src, int H, int nb_src, int r, int32_t *dst, int nb);
+
+/*
  * Block-sparse attention forward on `stream`.
+ *
+ * Implements [BB] section "BigBird：从二次方注意力到线性稀疏注意力": Q, K, V
+ * are cut into blocks of `block` tokens; query blocks 0 and nb-1 attend every
+ * key block; every middle query block i attends key blocks 0 and nb-1, the
+ * window {i-1, i, i+1} and the r blocks rand_attn[h][i-1]; padded keys get an
+ * additive -10000 before the row softmax; out = softmax(scores) V per row.
+ * [BP] sections "三类注意力组合全局 局部 随机" (the same three parts, rows 1
+ * and nb-2 included), "序列长度的块对齐要求" (L must be a multiple of the
+ * block: BBSA_ERR_SHAPE), "序列过短时的自动回退" (full attention when
+ * L <= (5 + 2r) * block) and "使用限制与注意事项" (r >= 1).
  *
  * q, k, v:   device, [B, H, L, d] of `dtype`, 16-byte aligned (as are out
  *            and mask; rand_attn 4-byte aligned), else BBSA_ERR_ARG.
@@ -112,32 +149,43 @@ int bbsa_check_rand_attn(const int32_t *rand_attn, int H, int nb, int r);
  *
  * Limits (BBSA_ERR_UNSUPPORTED beyond them): d = 64; block 64 or 128;
  * on the sparse path 5 + r <= 64 (a middle row attends at most 64 key
- * blocks); B * H * L * d <= 2^40 elements; at most 2^31 - 1 workgroups.
+ * blocks); L <= 2^24; B * H * L * d <= 2^40 elements; at most 2^31 - 1
+ * workgroups; (key chunks per full row) * nb < 2^31, i.e. about
+ * L <= 11.8 million tokens for bf16 with block 64.
  *
  * Returns BBSA_OK, or BBSA_OK_FULL_FALLBACK when L <= (5 + 2r) * block (every
  * query block then attends every key block), or a negative error code.  All
- * argument checks happen before any HIP call.  The library-owned workspace
- * (used only when a full row needs more than one partial, see above) is
- * allocated or grown on first use for a shape, which synchronises the
- * device; such calls that overlap on one device through different streams
- * must not race on it (the library serialises its own bookkeeping with a
- * mutex, not the kernels).  Calls that need no workspace (bf16 with
- * L <= 4096) share nothing.
+ * argument checks happen before any HIP call.
+ *
+ * Workspace: rows that leave more than one split-K partial (bf16 rows longer
+ * than 4096 keys; fp32 rows longer than 256 keys, and in fp32 calls with
+ * fewer than 2048 wavefronts of work full rows longer than 128 keys and
+ * every middle row) use a library-owned workspace, one per (device, stream).
+ * Calls on one stream are ordered by the stream; calls on different streams
+ * use different workspaces and may overlap.  A workspace is allocated or
+ * grown (powers of two, at least 1 MiB) with hipMalloc on the first call
+ * that needs more; the outgrown buffer stays allocated until
+ * bbsa_release_workspace.  Growth while `stream` is being captured into a
+ * graph returns BBSA_ERR_CAPTURE: make one eager call of the shape first.
  *
  * Graph capture: a call enqueues kernel launches only (no memset, no copy,
- * no host synchronisation), so it can be recorded into a HIP graph once the
- * workspace is large enough, e.g. after one eager call of the same shape;
- * replays then reuse the captured pointers.  Kernel timing must be off
- * during capture.
+ * no host synchronisation), so once its workspace is large enough it can be
+ * recorded into a HIP graph; replays use the captured buffers, which stay
+ * valid until bbsa_release_workspace (that call invalidates such graphs).
+ * Kernel timing must be off during capture.
  */
 int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
                  const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
-                 void *out, hipStream_t stream, int dtype);
+                 void *out, hipStream_t stream, bbsa_dtype dtype);
 
 /* Static string describing a status code. */
 const char *bbsa_status_string(int status);
 
-/* Free the library-owned workspace on every device. */
+/*
+ * Free every library-owned workspace (current and outgrown) on every device,
+ * after synchronising each device that has one.  Graphs captured with calls
+ * that used a workspace must not be replayed afterwards.
+ */
 void bbsa_release_workspace(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -147,13 +195,39 @@ int bbsa_version(void);
  * Kernel timing for benchmarks.  When enabled, bbsa_forward records a pair of
  * HIP events on `stream` around its main attention kernel and around its
  * split-K combine kernel when one runs (combine_ms counts 0 otherwise).
- * bbsa_timing_read synchronises on the recorded
- * events, returns the summed durations in milliseconds and the number of
- * timed calls, then clears the record.  At most 4096 calls are recorded
- * between reads; later calls are not timed.
+ * bbsa_timing_read synchronises on the recorded events, returns the summed
+ * durations in milliseconds and the number of timed calls, then clears the
+ * record.  At most 4096 calls are recorded between reads; later calls are
+ * not timed.  The record is guarded by a lock: calls from several threads
+ * are counted correctly (they are serialised while timing is on).
  */
 int bbsa_timing_enable(int enable);
 int bbsa_timing_read(double *main_ms, double *combine_ms, int *calls);
+
+/*
+ * Work decomposition of a forward call (a query for tests and tools; no HIP
+ * call).  For the shape and dtype of a bbsa_forward call with host plan
+ * `rand_attn` (may be NULL on the fallback), runs on the host the same item
+ * mapping and key-list construction the kernels run, and writes one record
+ * of BBSA_WORK_RECORD_INTS int32 per work item (a 64-row query tile against
+ * a key list) of the attention kernel:
+ *   [0] workgroup  [1] wavefront  [2] 0 (reserved)
+ *   [3] batch*H+head  [4] query block  [5] query tile  [6] full-row index
+ *   (-1 for a middle row)  [7] key chunk (full row) or key part (middle row)
+ *   [8], [9] first and one-past-last key-list position the unit walks
+ *   [10] 32-key steps per block  [11] chunks per full row  [12] partials per
+ *   full row left for the merge kernel  [13] key parts per middle row
+ *   [14], [15] unused (-1)  [16 + t] key block at list position t for
+ *   t in [rec[8], rec[9]), else -1.
+ * records: host buffer of capacity * BBSA_WORK_RECORD_INTS int32, or NULL to
+ * count only; at most `capacity` records are written.  *count receives the
+ * number of items, *grid the attention kernel's workgroup count.  Returns
+ * what bbsa_forward would return for the shape (pointer arguments aside).
+ */
+#define BBSA_WORK_RECORD_INTS 80
+int bbsa_work_map(int B, int H, int L, int d, int block, int r, bbsa_dtype dtype,
+                  const int32_t *rand_attn, int32_t *records, int64_t capacity,
+                  int64_t *count, int64_t *grid);
 
 #ifdef __cplusplus
 }

@@ -19,14 +19,16 @@ header; every function here is pinned by a ``-m "not gpu"`` test against
 something other than itself (brute force, a library routine, closed forms,
 invariants or a published test vector).
 """
-from .planner import SplitMix64, plan_rand_attn, check_rand_attn, candidate_blocks
+from .planner import (SplitMix64, plan_rand_attn, check_rand_attn, candidate_blocks, cap_block,
+                      truncate_plan)
 from .attention import (
     block_mask, token_mask, key_bias, uses_full_fallback, forward, full_attention,
     attended_key_counts,
 )
 
 __all__ = [
-    "SplitMix64", "plan_rand_attn", "check_rand_attn", "candidate_blocks",
+    "SplitMix64", "plan_rand_attn", "check_rand_attn", "candidate_blocks", "cap_block",
+    "truncate_plan",
     "block_mask", "token_mask", "key_bias", "uses_full_fallback", "forward",
     "full_attention", "attended_key_counts",
 ]

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, 1, -1, -2, -3, -4, -5):
+    for code in (0, 1, -1, -2, -3, -4, -5, -6):
         assert bbsa.bbsa_status_string(code) and bbsa.bbsa_status_string(code) != "unknown status"
     assert bbsa.bbsa_status_string(42) == "unknown status"
     assert bbsa.bbsa_version() >= 100

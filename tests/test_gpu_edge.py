@@ -132,3 +132,30 @@ def test_workspace_regrows_and_releases():
             bbsa.bbsa_release_workspace()
     for i in range(len(results)):
         assert np.array_equal(outs[i], outs[i + len(results)]), f"case {i} changed across workspace reuse"
+
+
+def test_two_streams_with_workspace_run_concurrently():
+    # Two calls that both need the split-K workspace (rows of 8192 keys) run
+    # on two streams at once, several times, on different inputs; each
+    # stream has its own workspace, so both results must match the oracle.
+    announce("two streams, workspace")
+    cases = []
+    for i, seed in enumerate((41, 42)):
+        inp = workloads.make_case(1, 3, 8192, 64, seed, valid=(8192 - 300 * i,))
+        cplan, oplan = plans(3, 128, 3, seed)
+        dev = {n: to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v")}
+        dev["mask"] = to_dev(inp["mask"], torch.float32)
+        dev["ra"] = torch.from_numpy(cplan).cuda()
+        cases.append((inp, oplan, dev))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full_like(c[2]["q"], float("nan")) for c in cases]
+    for _ in range(4):
+        for s, (inp, oplan, dev), o in zip(streams, cases, outs):
+            with torch.cuda.stream(s):
+                _, st = bbsa.bbsa_forward(dev["q"], dev["k"], dev["v"], dev["mask"], dev["ra"], 64, 3, out=o)
+                assert st == bbsa.BBSA_OK
+    torch.cuda.synchronize()
+    for (inp, oplan, dev), o in zip(cases, outs):
+        want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64)
+        assert_close(o.float().cpu().numpy().astype(np.float64), want, "bf16", "two streams")

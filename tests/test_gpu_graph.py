@@ -43,16 +43,19 @@ def test_graph_replay_matches_eager(B, H, L, block, r, dtype):
     mask = to_dev(inp["mask"], torch.float32)
     ra = torch.from_numpy(cplan).cuda()
 
-    # Eager call first: it also sizes the library workspace, so the captured
-    # call allocates nothing.
-    eager_out, st = bbsa.bbsa_forward(q, k, v, mask, ra, block, r)
+    # Eager call first, on the stream the capture will use: it sizes that
+    # stream's library workspace, so the captured call allocates nothing.
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):
+        eager_out, st = bbsa.bbsa_forward(q, k, v, mask, ra, block, r)
     assert st == bbsa.BBSA_OK
     torch.cuda.synchronize()
     eager = eager_out.float().cpu().numpy()
 
     out = torch.empty_like(q)
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=cap_stream):
         _, st_cap = bbsa.bbsa_forward(q, k, v, mask, ra, block, r, out=out)
     assert st_cap == bbsa.BBSA_OK
     torch.cuda.synchronize()
@@ -68,3 +71,50 @@ def test_graph_replay_matches_eager(B, H, L, block, r, dtype):
     blocks = sample_blocks(nb)
     want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block, query_blocks=blocks)
     assert_close(gather_rows(got.astype(np.float64), blocks, block), want, dtype, "graph replay vs oracle")
+
+
+def _hip():
+    import ctypes
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    h.hipStreamBeginCapture.restype = ctypes.c_int
+    h.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    h.hipStreamEndCapture.restype = ctypes.c_int
+    h.hipGraphDestroy.argtypes = [ctypes.c_void_p]
+    h.hipGraphDestroy.restype = ctypes.c_int
+    return h
+
+
+def test_workspace_growth_during_capture_is_refused():
+    # A stream that has never run a call needing the workspace is captured
+    # (relaxed mode, HIP's own API): the call must return BBSA_ERR_CAPTURE
+    # before touching the stream, and the capture must still end cleanly.
+    import ctypes
+    announce("capture without a sized workspace")
+    inp = workloads.make_case(1, 2, 8192, 64, 33)
+    plan = bbsa.bbsa_plan_rand_attn(2, 128, 3, 33)
+    q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    ra = torch.from_numpy(plan).cuda()
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    hip = _hip()
+    HIP_CAPTURE_RELAXED = 2
+    assert hip.hipStreamBeginCapture(ctypes.c_void_p(s.cuda_stream), HIP_CAPTURE_RELAXED) == 0
+    st = bbsa.lib().bbsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), None, ra.data_ptr(),
+                                 1, 2, 8192, 64, 64, 3, out.data_ptr(), ctypes.c_void_p(s.cuda_stream),
+                                 bbsa.BBSA_BF16)
+    graph = ctypes.c_void_p()
+    assert hip.hipStreamEndCapture(ctypes.c_void_p(s.cuda_stream), ctypes.byref(graph)) == 0
+    if graph.value:
+        hip.hipGraphDestroy(graph)
+    assert st == bbsa.BBSA_ERR_CAPTURE
+    # The same stream works eagerly afterwards.
+    with torch.cuda.stream(s):
+        got, st2 = bbsa.bbsa_forward(q, k, v, None, ra, 64, 3)
+    s.synchronize()
+    assert st2 == bbsa.BBSA_OK
+    blocks = sample_blocks(128)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], None, plan, 64, query_blocks=blocks)
+    assert_close(gather_rows(got.float().cpu().numpy().astype(np.float64), blocks, 64), want, "bf16",
+                 "eager after refused capture")

@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
 
-Small cases are compared over every output element; the five workloads at
-their full sizes are compared on every row of sampled query blocks (both
-global rows, their neighbours and middle rows), in the same launch
-configuration the benchmark times.
+Small cases are compared over every output element.  The five workloads run
+at their full sizes in the launch configuration the benchmark times: the
+first three are compared on every row, the two longest on every row of two
+(batch, head) pairs and on sampled query blocks of every other pair; the
+rows inside each sequence's valid length are also reported on their own.
+Output buffers start as NaN, so a row the kernels never write fails.
 """
 import numpy as np
 import pytest
@@ -11,8 +13,8 @@ import torch
 
 import oracle
 from block_sparse_long_bbsa_amd import bbsa, workloads
-from gpu_helpers import (announce, assert_close, gather_rows, plans, run_gpu, sample_blocks,
-                         to_dev)
+from gpu_helpers import (announce, assert_close, gather_rows, oracle_slices, plans, run_gpu,
+                         sample_blocks, to_dev, valid_query_rows, varied_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,6 +138,38 @@ def test_fully_padded_sequence_matches_oracle():
     assert_close(got, want, "bf16", "fully padded")
 
 
+@pytest.mark.parametrize("B,H,L,block,valid", [
+    (1, 2, 1024, 64, (0,)),          # every key padded: a constant -10000 on every score
+    (2, 2, 2048, 128, (0, 2048)),    # one fully padded sequence next to an unpadded one
+])
+def test_f32_fully_padded_sequence_matches_oracle(B, H, L, block, valid):
+    announce(f"f32 fully padded B{B} H{H} L{L} block{block} valid={valid}")
+    inp = workloads.make_case(B, H, L, 64, 19, dtype="f32", valid=valid)
+    r = 3 if block == 64 else 2
+    cplan, oplan = plans(H, L // block, r, 19)
+    got, _ = run_gpu(inp, block, r, "f32", cplan)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block)
+    assert_close(got, want, "f32", f"f32 fully padded L{L}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_padded_query_rows_match_oracle(dtype):
+    # Valid lengths that end inside a block: the query rows past the valid
+    # length are computed with the same formula (key-side masking only) and
+    # compared like every other row; the valid rows are reported on their own.
+    announce(f"padded query rows {dtype}")
+    B, H, L = 3, 2, 2048
+    valid = (1000, 1537, 64)
+    inp = workloads.make_case(B, H, L, 64, 20, dtype=dtype, valid=valid)
+    cplan, oplan = plans(H, L // 64, 3, 20)
+    got, _ = run_gpu(inp, 64, 3, dtype, cplan)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64)
+    assert_close(got, want, dtype, f"padded query rows {dtype} all rows")
+    for b, n in enumerate(valid):
+        assert_close(got[b, :, n:], want[b, :, n:], dtype, f"padded query rows {dtype} b{b} padded rows")
+        assert_close(got[b, :, :n], want[b, :, :n], dtype, f"padded query rows {dtype} b{b} valid rows")
+
+
 def test_out_of_range_plan_stays_in_bounds():
     # Indices are clamped: no fault, finite output (result unspecified).
     announce("clamped plan")
@@ -162,6 +196,14 @@ def test_output_guard_regions_untouched():
     assert_close(out.float().cpu().numpy().astype(np.float64), want, "bf16", "guarded")
 
 
+# Full-size workloads, in the launch configuration the benchmark times.
+# C1-C3: every row of every (batch, head).  C4, C5: every row of two
+# (batch, head) pairs that the kernel maps to different XCD lanes (pair x
+# runs on lane x mod 8), plus both global rows, their neighbours and six
+# middle blocks drawn per pair on every other pair.
+FULL_PAIRS = {4: (0, 9), 5: (0, 15)}
+
+
 @pytest.mark.parametrize("wid,seed", [(1, None), (2, None), (3, None), (3, 1), (4, None), (5, None)])
 def test_workload_parity(wid, seed):
     w = workloads.WORKLOADS[wid]
@@ -171,13 +213,27 @@ def test_workload_parity(wid, seed):
     cplan, oplan = plans(w.H, w.nb, w.r, plan_seed)
     got, st = run_gpu(inp, w.block, w.r, w.dtype, cplan)
     assert st == bbsa.BBSA_OK
-    if wid == 1:
-        want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, w.block)
-        assert_close(got, want, w.dtype, w.name)
-        return
-    blocks = sample_blocks(w.nb)
-    want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, w.block,
-                          query_blocks=blocks)
-    assert_close(gather_rows(got, blocks, w.block), want, w.dtype, f"{w.name} sampled")
-    # valid rows only (rows past the valid length are discarded by callers)
-    assert np.isfinite(got).all()
+    # Every output row was written (the buffer started as NaN).
+    assert np.isfinite(got).all(), "non-finite output: some row was not written"
+    full = FULL_PAIRS.get(wid)
+    jobs = []
+    for b in range(w.B):
+        for h in range(w.H):
+            bh = b * w.H + h
+            qbs = None if full is None or bh in full else varied_blocks(w.nb, bh)
+            jobs.append((b, h, qbs))
+    wants = oracle_slices(inp, oplan, w.block, jobs)
+    g_all, w_all, g_valid, w_valid = [], [], [], []
+    for (b, h, qbs), want in zip(jobs, wants):
+        blocks = range(w.nb) if qbs is None else qbs
+        rows = np.concatenate([np.arange(i * w.block, (i + 1) * w.block) for i in blocks])
+        g = got[b, h, rows]
+        g_all.append(g)
+        w_all.append(want)
+        keep = valid_query_rows(inp["mask"], b, rows)
+        g_valid.append(g[keep])
+        w_valid.append(want[keep])
+    g_all, w_all = np.concatenate(g_all), np.concatenate(w_all)
+    assert_close(g_all, w_all, w.dtype, f"{w.name} seed{plan_seed} all rows")
+    g_valid, w_valid = np.concatenate(g_valid), np.concatenate(w_valid)
+    assert_close(g_valid, w_valid, w.dtype, f"{w.name} seed{plan_seed} valid rows")

@@ -150,3 +150,87 @@ def test_golden_plan_fixture():
     rows = [list(map(int, ln.split())) for ln in open(path) if ln.strip() and not ln.startswith("#")]
     want = np.array(rows, dtype=np.int32).reshape(3, 14, 3)
     assert np.array_equal(plan_rand_attn(3, 16, 3, 1), want)
+
+
+# ---- the last_idx cap ("models 仓库中的 BigBird…", section "随机块掩码是如何生成的":
+# random blocks only within the first 1024 tokens; the plan of the maximum
+# length serves shorter sequences through its first rows).
+
+from oracle.planner import cap_block, truncate_plan  # noqa: E402
+
+
+def test_cap_block_closed_form():
+    assert cap_block(64, 64, 1024) == 15          # blocks 0..15 hold tokens 0..1023
+    assert cap_block(64, 64, 1087) == 15          # block 16 would end at token 1088
+    assert cap_block(64, 64, 1088) == 16
+    assert cap_block(256, 128, 1024) == 7
+    assert cap_block(64, 64, 0) == 62 and cap_block(64, 64, None) == 62
+    assert cap_block(20, 64, 1 << 20) == 18        # never past the last middle block
+
+
+def test_capped_candidates_explicit():
+    # nb = 20, block 64, last_idx 384: blocks 1..5 allowed.
+    assert candidate_blocks(20, 1, 64, 384) == [3, 4, 5]
+    assert candidate_blocks(20, 2, 64, 384) == [4, 5]
+    assert candidate_blocks(20, 4, 64, 384) == [1, 2]
+    assert candidate_blocks(20, 6, 64, 384) == [1, 2, 3, 4]
+    assert candidate_blocks(20, 12, 64, 384) == [1, 2, 3, 4, 5]
+    assert candidate_blocks(20, 12) == [c for c in range(1, 19) if abs(c - 12) > 1]
+
+
+def test_capped_plan_exhausts_rows_with_exactly_r_candidates():
+    # r = 2 under the cap above: rows 2, 3 and 4 have exactly two candidates,
+    # so they must pick exactly those, in some order.
+    plan = plan_rand_attn(4, 20, 2, 9, block=64, last_idx=384)
+    for h in range(4):
+        assert set(plan[h, 1]) == {4, 5}
+        assert set(plan[h, 2]) == {1, 5}
+        assert set(plan[h, 3]) == {1, 2}
+    assert check_rand_attn(plan, 20, 2, block=64, last_idx=384) == []
+    assert plan.max() <= 5
+
+
+def test_capped_plan_invariants_and_inactive_cap():
+    for seed in range(5):
+        capped = plan_rand_attn(3, 64, 3, seed, block=64, last_idx=1024)
+        assert check_rand_attn(capped, 64, 3, block=64, last_idx=1024) == []
+        assert capped.max() <= 15 and capped.min() >= 1
+        # A cap at or past the last middle block changes nothing.
+        for li in (63 * 64, 1 << 20, 0, None):
+            assert np.array_equal(plan_rand_attn(3, 64, 3, seed, block=64, last_idx=li),
+                                  plan_rand_attn(3, 64, 3, seed))
+    # The same plan violates a lower cap, and an uncapped plan violates this one.
+    capped = plan_rand_attn(3, 64, 3, 1, block=64, last_idx=1024)
+    assert check_rand_attn(capped, 64, 3, block=64, last_idx=512) != []
+    assert check_rand_attn(plan_rand_attn(3, 64, 3, 1), 64, 3, block=64, last_idx=1024) != []
+
+
+def test_capped_pick_frequencies_are_uniform():
+    # Row 40 of nb = 64 under last_idx 1024: 15 candidates (blocks 1..15),
+    # each picked with probability 3/15 over many seeds (chi-square, loose).
+    counts = np.zeros(16)
+    n = 600
+    for seed in range(n):
+        for c in plan_rand_attn(1, 64, 3, seed, block=64, last_idx=1024)[0, 39]:
+            counts[c] += 1
+    exp = n * 3 / 15
+    chi2 = ((counts[1:] - exp) ** 2 / exp).sum()
+    assert counts[0] == 0 and chi2 < 45.0      # 14 degrees of freedom; p ~ 5e-5
+
+
+def test_capped_plan_too_low_cap_raises():
+    with pytest.raises(ValueError):
+        plan_rand_attn(1, 64, 3, 0, block=64, last_idx=256)
+    with pytest.raises(ValueError):
+        plan_rand_attn(1, 64, 3, 0, last_idx=1024)      # a cap needs the block size
+
+
+def test_truncated_plan_serves_shorter_sequences():
+    big = plan_rand_attn(2, 64, 3, 3, block=64, last_idx=1024)
+    for nb in (17, 20, 40):
+        small = truncate_plan(big, nb)
+        assert small.shape == (2, nb - 2, 3)
+        assert np.array_equal(small, big[:, :nb - 2])
+        assert check_rand_attn(small, nb, 3) == []
+    # Uncapped picks reach past a shorter sequence's middle blocks.
+    assert check_rand_attn(truncate_plan(plan_rand_attn(2, 64, 3, 3), 20), 20, 3) != []

@@ -55,3 +55,49 @@ def test_c_planner_argument_errors(lib):
     with pytest.raises(bbsa.BbsaError) as e:
         bbsa.bbsa_plan_rand_attn(1, 16, 0, 0)
     assert e.value.status == bbsa.BBSA_ERR_ARG
+
+
+# The last_idx cap ("models 仓库中的 BigBird…", section "随机块掩码是如何生成的").
+@pytest.mark.parametrize("H", [1, 12])
+@pytest.mark.parametrize("nb,r,block,last_idx", [
+    (64, 3, 64, 1024), (64, 3, 64, 0), (64, 3, 64, 4096), (64, 3, 64, 1 << 20), (256, 2, 128, 1024),
+    (256, 3, 64, 1024), (16, 1, 64, 640), (40, 5, 128, 2048), (64, 3, 64, 1087), (64, 2, 64, 448),
+])
+def test_c_capped_planner_matches_oracle(lib, H, nb, r, block, last_idx):
+    for seed in (0, 1, 13, 2**63 + 5):
+        c = bbsa.bbsa_plan_rand_attn_capped(H, nb, r, seed, block, last_idx)
+        o = oracle_plan(H, nb, r, seed, block=block, last_idx=last_idx)
+        assert np.array_equal(c, o), (H, nb, r, block, last_idx, seed)
+        assert bbsa.bbsa_check_rand_attn_capped(c, nb, r, block, last_idx) == bbsa.BBSA_OK
+
+
+def test_c_capped_planner_errors(lib):
+    # A cap of block 3 leaves row 2 only block... fewer than r = 3 candidates.
+    with pytest.raises(bbsa.BbsaError) as e:
+        bbsa.bbsa_plan_rand_attn_capped(1, 64, 3, 0, 64, 4 * 64)
+    assert e.value.status == bbsa.BBSA_ERR_SHAPE
+    with pytest.raises(bbsa.BbsaError) as e:
+        bbsa.bbsa_plan_rand_attn_capped(1, 64, 3, 0, 0, 1024)
+    assert e.value.status == bbsa.BBSA_ERR_ARG
+
+
+def test_c_capped_check_rejects_picks_past_the_cap(lib):
+    ra = bbsa.bbsa_plan_rand_attn(2, 64, 3, 4)           # uncapped: picks up to block 62
+    assert ra.max() > 15
+    assert bbsa.bbsa_check_rand_attn_capped(ra, 64, 3, 64, 1024) == bbsa.BBSA_ERR_PLAN
+    capped = bbsa.bbsa_plan_rand_attn_capped(2, 64, 3, 4, 64, 1024)
+    bad = capped.copy(); bad[1, 40, 2] = 16              # one past the cap (block 15)
+    assert bbsa.bbsa_check_rand_attn_capped(bad, 64, 3, 64, 1024) == bbsa.BBSA_ERR_PLAN
+
+
+def test_c_truncate_matches_oracle(lib):
+    from oracle.planner import truncate_plan, check_rand_attn
+    big = bbsa.bbsa_plan_rand_attn_capped(3, 64, 3, 7, 64, 1024)
+    for nb in (17, 32, 63):
+        st, small = bbsa.bbsa_truncate_rand_attn(big, nb)
+        assert st == bbsa.BBSA_OK
+        assert np.array_equal(small, truncate_plan(big, nb))
+        assert check_rand_attn(small, nb, 3) == []
+    # An uncapped plan's rows reach past a shorter sequence: refused.
+    st, _ = bbsa.bbsa_truncate_rand_attn(bbsa.bbsa_plan_rand_attn(3, 64, 3, 7), 32)
+    assert st == bbsa.BBSA_ERR_PLAN
