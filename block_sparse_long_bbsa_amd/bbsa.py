@@ -24,6 +24,7 @@ BBSA_ERR_UNSUPPORTED = -3
 BBSA_ERR_HIP = -4
 BBSA_ERR_PLAN = -5
 BBSA_ERR_CAPTURE = -6
+BBSA_ERR_SCRATCH = -7
 
 WORK_RECORD_INTS = 80
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.bbsa_forward.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + \
             [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         L.bbsa_forward.restype = ctypes.c_int
+        L.bbsa_forward_noalloc.argtypes = L.bbsa_forward.argtypes
+        L.bbsa_forward_noalloc.restype = ctypes.c_int
         L.bbsa_status_string.argtypes = [ctypes.c_int]
         L.bbsa_status_string.restype = ctypes.c_char_p
         L.bbsa_release_workspace.argtypes = []
@@ -152,16 +155,8 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
-def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=None,
-                 warn_fallback: bool = True):
-    """Block-sparse attention forward on the GPU.
-
-    q, k, v: contiguous ``[B, H, L, d]`` bf16 or fp32 GPU tensors.
-    mask: float32 ``[B, L]`` GPU tensor or None.  rand_attn: int32
-    ``[H, nb-2, r]`` GPU tensor (may be None when L <= (5+2r)*block).
-    Returns ``(out, status)``; status 1 means full attention was computed
-    (a warning is issued, as the reference layer does).
-    """
+def _marshal(q, k, v, mask, rand_attn, block, r, out, stream):
+    """Check the tensors and return the C arguments of a forward call."""
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
@@ -173,9 +168,7 @@ def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=
         raise ValueError("q, k, v must share one dtype")
     B, H, L, d = q.shape
     code = _dtype_code(q)
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
         raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
     mptr = None
     if mask is not None:
@@ -193,16 +186,51 @@ def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    with torch.cuda.device(q.device):
-        st = lib().bbsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, rptr,
-                                B, H, L, d, int(block), int(r), out.data_ptr(),
-                                ctypes.c_void_p(handle), code)
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, rptr, B, H, L, d, int(block), int(r),
+            out.data_ptr(), ctypes.c_void_p(handle), code)
+
+
+def _status(st, where, L, block, r, warn_fallback):
     if st < 0:
-        if st in (BBSA_ERR_HIP, BBSA_ERR_CAPTURE):
-            raise BbsaError(st, "bbsa_forward")
-        raise ValueError(f"bbsa_forward: status {st}: {bbsa_status_string(st)}")
+        if st in (BBSA_ERR_HIP, BBSA_ERR_CAPTURE, BBSA_ERR_SCRATCH):
+            raise BbsaError(st, where)
+        raise ValueError(f"{where}: status {st}: {bbsa_status_string(st)}")
     if st == BBSA_OK_FULL_FALLBACK and warn_fallback:
         warnings.warn(f"sequence length {L} <= (5 + 2*{r}) * {block}: computed full attention")
+
+
+def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=None,
+                 warn_fallback: bool = True):
+    """Block-sparse attention forward on the GPU.
+
+    q, k, v: contiguous ``[B, H, L, d]`` bf16 or fp32 GPU tensors.
+    mask: float32 ``[B, L]`` GPU tensor or None.  rand_attn: int32
+    ``[H, nb-2, r]`` GPU tensor (may be None when L <= (5+2r)*block).
+    Returns ``(out, status)``; status 1 means full attention was computed
+    (a warning is issued, as the reference layer does).
+    """
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    args = _marshal(q, k, v, mask, rand_attn, block, r, out, stream)
+    with torch.cuda.device(q.device):
+        st = lib().bbsa_forward(*args)
+    _status(st, "bbsa_forward", q.shape[2], block, r, warn_fallback)
+    return out, st
+
+
+def bbsa_forward_noalloc(q, k, v, mask, rand_attn, block: int, r: int, out, stream=None,
+                         warn_fallback: bool = True):
+    """``bbsa_forward`` through the entry point that allocates nothing (the
+    library's fixed per-device scratch; see include/bbsa.h).  ``out`` must be
+    given.  Returns ``(out, status)``."""
+    import torch
+    if out is None:
+        raise ValueError("bbsa_forward_noalloc needs an output tensor")
+    args = _marshal(q, k, v, mask, rand_attn, block, r, out, stream)
+    with torch.cuda.device(q.device):
+        st = lib().bbsa_forward_noalloc(*args)
+    _status(st, "bbsa_forward_noalloc", q.shape[2], block, r, warn_fallback)
     return out, st
 
 

@@ -1001,20 +1001,9 @@ int ensure_workspace(size_t bytes, hipStream_t stream, float **ws) {
   return BBSA_OK;
 }
 
-}  // namespace
-
-extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
-                            const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
-                            void *out, hipStream_t stream, bbsa_dtype dtype) {
-  Launch ln;
-  const int st = setup_forward(q, k, v, mask, rand_attn, B, H, L, d, block, r, out, (int)dtype, &ln);
-  if (st < 0) return st;
-  Params &p = ln.p;
-  if (ln.n_partials > 0) {
-    const int rc = ensure_workspace((size_t)ln.n_partials * kPartialFloats * sizeof(float), stream, &p.ws);
-    if (rc != BBSA_OK) return rc;
-  }
-
+// Enqueue the kernels of a validated call (its workspace pointer set).
+int launch_forward(const Launch &ln, const float *mask, hipStream_t stream, bbsa_dtype dtype, int status) {
+  const Params &p = ln.p;
   std::unique_lock<std::mutex> tlock(g_timing.mu);
   const bool timed = g_timing.enabled && g_timing.n < kMaxTimed;
   const int tslot = g_timing.n;
@@ -1043,7 +1032,67 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
     if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
     if (timed && hipEventRecord(g_timing.ev[tslot][3], stream) != hipSuccess) return BBSA_ERR_HIP;
   }
-  return st;
+  return status;
+}
+
+// Fixed split-K scratch of bbsa_forward_noalloc: one array per device, held
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it only stands in for the symbol): the device address
+// is looked up once per device with hipGetSymbolAddress and kept here.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;                 // guards g_scratch_ptr
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with that device current).
+int scratch_address(float **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BBSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BBSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return BBSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (float *)g_scratch_ptr[dev];
+  return BBSA_OK;
+}
+
+}  // namespace
+
+extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
+                            const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
+                            void *out, hipStream_t stream, bbsa_dtype dtype) {
+  Launch ln;
+  const int st = setup_forward(q, k, v, mask, rand_attn, B, H, L, d, block, r, out, (int)dtype, &ln);
+  if (st < 0) return st;
+  if (ln.n_partials > 0) {
+    const int rc = ensure_workspace((size_t)ln.n_partials * kPartialFloats * sizeof(float), stream, &ln.p.ws);
+    if (rc != BBSA_OK) return rc;
+  }
+  return launch_forward(ln, mask, stream, dtype, st);
+}
+
+extern "C" int bbsa_forward_noalloc(const void *q, const void *k, const void *v, const float *mask,
+                                    const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
+                                    void *out, hipStream_t stream, bbsa_dtype dtype) {
+  Launch ln;
+  const int st = setup_forward(q, k, v, mask, rand_attn, B, H, L, d, block, r, out, (int)dtype, &ln);
+  if (st < 0) return st;
+  if (ln.n_partials > 0) {
+    if ((size_t)ln.n_partials * kPartialFloats * sizeof(float) > kScratchBytes) return BBSA_ERR_SCRATCH;
+    const int rc = scratch_address(&ln.p.ws);
+    if (rc != BBSA_OK) return rc;
+  }
+  return launch_forward(ln, mask, stream, dtype, st);
 }
 
 extern "C" const char *bbsa_status_string(int status) {
@@ -1056,6 +1105,7 @@ extern "C" const char *bbsa_status_string(int status) {
     case BBSA_ERR_HIP: return "HIP runtime error";
     case BBSA_ERR_PLAN: return "rand_attn violates the plan invariants";
     case BBSA_ERR_CAPTURE: return "the workspace must grow while the stream is being captured (run one eager call of this shape first)";
+    case BBSA_ERR_SCRATCH: return "the call needs more split-K scratch than bbsa_forward_noalloc's fixed 16 MiB";
     default: return "unknown status";
   }
 }

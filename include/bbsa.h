@@ -45,7 +45,8 @@ enum {
   BBSA_ERR_UNSUPPORTED = -3, /* d != 64, block not in {64, 128}, unknown dtype, too large */
   BBSA_ERR_HIP = -4,         /* a HIP call or kernel launch failed */
   BBSA_ERR_PLAN = -5,        /* rand_attn violates an invariant (bbsa_check_rand_attn) */
-  BBSA_ERR_CAPTURE = -6      /* the workspace would have to grow during stream capture */
+  BBSA_ERR_CAPTURE = -6,     /* the workspace would have to grow during stream capture */
+  BBSA_ERR_SCRATCH = -7      /* bbsa_forward_noalloc: more split-K scratch than its fixed maximum */
 };
 
 /*
@@ -177,6 +178,26 @@ int bbsa_truncate_rand_attn(const int32_t *src, int H, int nb_src, int r, int32_
 int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
                  const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
                  void *out, hipStream_t stream, bbsa_dtype dtype);
+
+/*
+ * bbsa_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, computation, results and errors as bbsa_forward; the
+ * split-K partials (the only device memory beyond inputs and outputs) go to a
+ * fixed 16 MiB array that the library holds on each device it runs on until
+ * the process ends, so the call itself allocates nothing.  That fits 1007
+ * partials of 16.3 KiB: every bf16 call with L <= 4096 (none needed), and
+ * e.g. B * H * 2 * (L / 4096) <= 1007 bf16 row tiles of block 64.  A call
+ * needing more returns BBSA_ERR_SCRATCH before any HIP call.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or different host threads) race and must be ordered by the
+ * caller; each call writes every partial it reads, so nothing needs clearing
+ * between calls.
+ */
+int bbsa_forward_noalloc(const void *q, const void *k, const void *v, const float *mask,
+                         const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
+                         void *out, hipStream_t stream, bbsa_dtype dtype);
 
 /* Static string describing a status code. */
 const char *bbsa_status_string(int status);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, 1, -1, -2, -3, -4, -5, -6):
+    for code in (0, 1, -1, -2, -3, -4, -5, -6, -7):
         assert bbsa.bbsa_status_string(code) and bbsa.bbsa_status_string(code) != "unknown status"
     assert bbsa.bbsa_status_string(42) == "unknown status"
     assert bbsa.bbsa_version() >= 100
@@ -71,3 +71,18 @@ def call(lib, B=1, H=1, L=1024, d=64, block=64, r=3, dtype=0, q=FAKE, k=FAKE, v=
 ])
 def test_forward_rejects_invalid_arguments(lib, kw, code):
     assert call(lib, **kw) == code
+
+
+def test_noalloc_validates_like_forward(lib):
+    # Same argument checks as bbsa_forward; a call whose partials would not fit
+    # the fixed scratch is refused with its own status.  No HIP call happens.
+    for kw, code in [(dict(q=None), -1), (dict(L=1000), -2), (dict(d=128), -3), (dict(ra=None), -1)]:
+        args = dict(B=1, H=1, L=1024, d=64, block=64, r=3, dtype=0, q=FAKE, k=FAKE, v=FAKE, out=FAKE, ra=FAKE,
+                    mask=None)
+        args.update(kw)
+        st = lib.bbsa_forward_noalloc(args["q"], args["k"], args["v"], args["mask"], args["ra"], args["B"],
+                                      args["H"], args["L"], args["d"], args["block"], args["r"], args["out"],
+                                      None, args["dtype"])
+        assert st == code
+    st = lib.bbsa_forward_noalloc(FAKE, FAKE, FAKE, None, FAKE, 8, 16, 32768, 64, 64, 3, FAKE, None, 0)
+    assert st == bbsa.BBSA_ERR_SCRATCH
