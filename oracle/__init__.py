@@ -23,12 +23,12 @@ from .planner import (SplitMix64, plan_rand_attn, check_rand_attn, candidate_blo
                       truncate_plan)
 from .attention import (
     block_mask, token_mask, key_bias, uses_full_fallback, forward, full_attention,
-    attended_key_counts,
+    attended_key_counts, pair_bias, forward_padded,
 )
 
 __all__ = [
     "SplitMix64", "plan_rand_attn", "check_rand_attn", "candidate_blocks", "cap_block",
     "truncate_plan",
     "block_mask", "token_mask", "key_bias", "uses_full_fallback", "forward",
-    "full_attention", "attended_key_counts",
+    "full_attention", "attended_key_counts", "pair_bias", "forward_padded",
 ]

@@ -40,10 +40,17 @@ Readings where the pages are silent:
 * the fallback threshold reads ``L <= (5 + 2r) * block`` (the "+" is lost in
   the page's text; 704 = (5 + 2*3) * 64 confirms it).
 
-Parity status: pinned (tests/test_oracle_attention.py) against scalar brute
-force on tiny inputs, against torch's scaled_dot_product_attention in
-float64, against closed forms (constant V, Q = 0, key shift, attended-key
-counts) and against invariants (row sums, exact zeros, batch independence).
+Also: the query x key masking mode (the pages' band mask is the outer
+product of the query-side and key-side masks), each row's log-sum-exp, and
+lengths that are not a multiple of the block (the encoder pads to the block
+and trims the output).
+
+Parity status: pinned (tests/test_oracle_attention.py,
+tests/test_oracle_extensions.py) against scalar brute force on tiny inputs,
+against torch's scaled_dot_product_attention and logsumexp in float64,
+against closed forms (constant V, Q = 0, key shift, attended-key counts,
+query x key rows with mask 1 or 0) and against invariants (row sums, exact
+zeros, batch independence, padding that changes nothing).
 """
 from __future__ import annotations
 
@@ -104,19 +111,43 @@ def _softmax_rows(S: np.ndarray) -> np.ndarray:
     return E / E.sum(axis=-1, keepdims=True)
 
 
+def pair_bias(mask_b, rows, L: int, query_key: bool = False) -> np.ndarray:
+    """Additive padding bias ``[len(rows), L]`` of one sequence for the query
+    rows ``rows``.
+
+    Key side (the default): ``-10000 * (1 - m[u])`` for every query row.
+    Query x key (``query_key``): ``-10000 * (1 - m[t] * m[u])``, the outer
+    product of the query-side and key-side masks that the pages' band mask
+    is built from ("models 仓库中的 BigBird…", section "随机块掩码是如何生成的":
+    BigBirdMasks forms the 3-D band mask from the from-mask and the to-mask by
+    an einsum).  ``mask_b`` None means every position is valid."""
+    rows = np.asarray(rows)
+    if mask_b is None:
+        return np.zeros((len(rows), L), dtype=np.float64)
+    m = np.asarray(mask_b, dtype=np.float64).reshape(L)
+    if not query_key:
+        return np.broadcast_to(PAD_BIAS * (1.0 - m)[None, :], (len(rows), L)).copy()
+    return PAD_BIAS * (1.0 - m[rows][:, None] * m[None, :])
+
+
 def forward(q, k, v, mask, rand_attn, block: int, query_blocks=None,
-            allow_fallback: bool = True, return_probs: bool = False):
+            allow_fallback: bool = True, return_probs: bool = False,
+            query_key_mask: bool = False, return_lse: bool = False):
     """Masked dense attention under the BigBird block mask, in float64.
 
     q, k, v: ``[B, H, L, d]`` (any real dtype; upcast exactly to float64).
-    mask: ``[B, L]`` values in [0, 1] (1 = valid key) or None.
+    mask: ``[B, L]`` values in [0, 1] (1 = valid) or None.
     rand_attn: ``[H, nb-2, r]`` integer plan, or None (no random blocks).
     query_blocks: iterable of query block indices to compute (default: all);
     the result then holds only those blocks' rows, in the order given.
     allow_fallback: apply the short-sequence fallback to full attention.
+    query_key_mask: bias -10000 * (1 - m[query] * m[key]) instead of the
+    key-side -10000 * (1 - m[key]) (see ``pair_bias``).
 
-    Returns ``out`` (float64 ``[B, H, rows, d]``), or ``(out, P)`` with the
-    probabilities ``[B, H, rows, L]`` when ``return_probs`` is set.
+    Returns ``out`` (float64 ``[B, H, rows, d]``); with ``return_probs`` also
+    the probabilities ``[B, H, rows, L]`` and with ``return_lse`` the natural
+    log-sum-exp of each row's scores over the keys it attends, bias included
+    (``[B, H, rows]``), in that order after ``out``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -127,27 +158,69 @@ def forward(q, k, v, mask, rand_attn, block: int, query_blocks=None,
     nb = L // block
     r = 0 if rand_attn is None else int(np.asarray(rand_attn).shape[2])
     full = allow_fallback and uses_full_fallback(L, block, r)
-    bias = key_bias(mask, B, L)
     qbs = list(range(nb)) if query_blocks is None else [int(i) for i in query_blocks]
     rows = len(qbs) * block
     out = np.empty((B, H, rows, d), dtype=np.float64)
     probs = np.empty((B, H, rows, L), dtype=np.float64) if return_probs else None
+    lse = np.empty((B, H, rows), dtype=np.float64) if return_lse else None
     for h in range(H):
         if full:
             M = np.ones((nb, nb), dtype=bool)
         else:
             M = block_mask(nb, None if rand_attn is None else np.asarray(rand_attn)[h])
         for b in range(B):
+            mb = None if mask is None else np.asarray(mask)[b]
             for n, i in enumerate(qbs):
+                qrows = np.arange(i * block, (i + 1) * block)
                 Qi = q[b, h, i * block:(i + 1) * block]          # [block, d]
-                S = Qi @ k[b, h].T + bias[b][None, :]           # [block, L]
+                S = Qi @ k[b, h].T + pair_bias(mb, qrows, L, query_key_mask)   # [block, L]
                 seen = np.repeat(M[i], block)                   # key tokens this block sees
                 S[:, ~seen] = -np.inf                           # outside the pattern: excluded
                 P = _softmax_rows(S)
                 out[b, h, n * block:(n + 1) * block] = P @ v[b, h]
                 if probs is not None:
                     probs[b, h, n * block:(n + 1) * block] = P
-    return (out, probs) if return_probs else out
+                if lse is not None:
+                    mx = S.max(axis=-1)
+                    lse[b, h, n * block:(n + 1) * block] = mx + np.log(np.exp(S - mx[:, None]).sum(axis=-1))
+    res = (out,)
+    if return_probs:
+        res += (probs,)
+    if return_lse:
+        res += (lse,)
+    return res if len(res) > 1 else out
+
+
+def forward_padded(q, k, v, mask, rand_attn, block: int, **kw):
+    """Forward for a length that need not be a multiple of the block.
+
+    "BigBirdPegasus…", section "序列长度的块对齐要求": the encoder pads its input
+    to a multiple of the block size and cuts the padding off the output.
+    Here the padding positions are zero vectors with mask 0 (so as keys they
+    get the -10000 bias like any padded key); the padded sequence goes
+    through ``forward`` and every result is cut back to the first L rows (and
+    the first L keys for the probabilities).  ``rand_attn`` is the plan of the
+    padded length, ``[H, ceil(L/block) - 2, r]``.  Keyword arguments go to
+    ``forward``."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, L, d = q.shape
+    Lp = -(-L // block) * block
+    pad = ((0, 0), (0, 0), (0, Lp - L), (0, 0))
+    m = np.ones((B, L)) if mask is None else np.asarray(mask, dtype=np.float64).reshape(B, L)
+    mp = np.concatenate([m, np.zeros((B, Lp - L))], axis=1)
+    res = forward(np.pad(q, pad), np.pad(k, pad), np.pad(v, pad), mp, rand_attn, block, **kw)
+    if not isinstance(res, tuple):
+        return res[:, :, :L]
+    out = [res[0][:, :, :L]]
+    i = 1
+    if kw.get("return_probs"):
+        out.append(res[i][:, :, :L, :L])
+        i += 1
+    if kw.get("return_lse"):
+        out.append(res[i][:, :, :L])
+    return tuple(out)
 
 
 def full_attention(q, k, v, mask):
