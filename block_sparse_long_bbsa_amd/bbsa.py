@@ -26,6 +26,9 @@ BBSA_ERR_PLAN = -5
 BBSA_ERR_CAPTURE = -6
 BBSA_ERR_SCRATCH = -7
 
+BBSA_FLAG_PAD_TO_BLOCK = 1
+BBSA_FLAG_QUERY_KEY_MASK = 2
+
 WORK_RECORD_INTS = 80
 
 _LIB = None
@@ -69,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.bbsa_forward.restype = ctypes.c_int
         L.bbsa_forward_noalloc.argtypes = L.bbsa_forward.argtypes
         L.bbsa_forward_noalloc.restype = ctypes.c_int
+        L.bbsa_forward_ex.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + \
+            [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint]
+        L.bbsa_forward_ex.restype = ctypes.c_int
         L.bbsa_status_string.argtypes = [ctypes.c_int]
         L.bbsa_status_string.restype = ctypes.c_char_p
         L.bbsa_release_workspace.argtypes = []
@@ -81,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.bbsa_timing_read.argtypes = [dp, dp, ctypes.POINTER(ctypes.c_int)]
         L.bbsa_timing_read.restype = ctypes.c_int
         i64p = ctypes.POINTER(ctypes.c_int64)
-        L.bbsa_work_map.argtypes = [ctypes.c_int] * 7 + [i32p, i32p, ctypes.c_int64, i64p, i64p]
+        L.bbsa_work_map.argtypes = [ctypes.c_int] * 7 + [ctypes.c_uint, i32p, i32p, ctypes.c_int64, i64p, i64p]
         L.bbsa_work_map.restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -155,7 +161,7 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
-def _marshal(q, k, v, mask, rand_attn, block, r, out, stream):
+def _marshal(q, k, v, mask, rand_attn, block, r, out, stream, pad=False):
     """Check the tensors and return the C arguments of a forward call."""
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -180,8 +186,9 @@ def _marshal(q, k, v, mask, rand_attn, block, r, out, stream):
     if rand_attn is not None:
         if not rand_attn.is_cuda or rand_attn.dtype != torch.int32 or not rand_attn.is_contiguous():
             raise ValueError("rand_attn must be a contiguous int32 GPU tensor")
-        if L % block == 0 and tuple(rand_attn.shape) != (H, L // block - 2, r):
-            raise ValueError(f"rand_attn must be [H, nb-2, r] = {(H, L // block - 2, r)}")
+        nb = -(-L // block)
+        if tuple(rand_attn.shape) != (H, nb - 2, r) and (L % block == 0 or pad):
+            raise ValueError(f"rand_attn must be [H, nb-2, r] = {(H, nb - 2, r)}")
         rptr = rand_attn.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
@@ -219,6 +226,35 @@ def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=
     return out, st
 
 
+def bbsa_forward_ex(q, k, v, mask, rand_attn, block: int, r: int, out=None, lse=None, stream=None,
+                    pad_to_block: bool = False, query_key_mask: bool = False, return_lse: bool = False,
+                    warn_fallback: bool = True):
+    """``bbsa_forward`` with options (see include/bbsa.h):
+
+    pad_to_block: L need not be a multiple of ``block`` (the sequence is
+    handled as padded to ceil(L/block) blocks; rand_attn is the plan of that
+    block count).  query_key_mask: bias -10000 (1 - m[query] m[key]).
+    return_lse / lse: also produce the float32 ``[B, H, L]`` row
+    log-sum-exp.  Returns ``(out, status)`` or ``(out, lse, status)``.
+    """
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    B, H, L, _ = q.shape
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, L] GPU tensor")
+    args = list(_marshal(q, k, v, mask, rand_attn, block, r, out, stream, pad=pad_to_block))
+    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0)
+    cargs = args[:12] + [None if lse is None else lse.data_ptr(), args[12], args[13], flags]
+    with torch.cuda.device(q.device):
+        st = lib().bbsa_forward_ex(*cargs)
+    _status(st, "bbsa_forward_ex", L, block, r, warn_fallback)
+    return (out, lse, st) if lse is not None else (out, st)
+
+
 def bbsa_forward_noalloc(q, k, v, mask, rand_attn, block: int, r: int, out, stream=None,
                          warn_fallback: bool = True):
     """``bbsa_forward`` through the entry point that allocates nothing (the
@@ -253,7 +289,8 @@ def bbsa_timing_read():
     return a.value, c.value, n.value
 
 
-def bbsa_work_map(B: int, H: int, L: int, d: int, block: int, r: int, dtype: int, rand_attn=None):
+def bbsa_work_map(B: int, H: int, L: int, d: int, block: int, r: int, dtype: int, rand_attn=None,
+                  flags: int = 0):
     """The attention kernel's work decomposition for a call's shape (see
     ``bbsa_work_map`` in include/bbsa.h): returns ``(status, grid, records)``
     with ``records`` an int32 array ``[units, 80]``."""
@@ -264,11 +301,11 @@ def bbsa_work_map(B: int, H: int, L: int, d: int, block: int, r: int, dtype: int
         ra = np.ascontiguousarray(rand_attn, dtype=np.int32)
         rptr = ra.ctypes.data_as(i32p)
     count, grid = ctypes.c_int64(), ctypes.c_int64()
-    st = lib().bbsa_work_map(B, H, L, d, block, r, dtype, rptr, None, 0, ctypes.byref(count),
+    st = lib().bbsa_work_map(B, H, L, d, block, r, dtype, flags, rptr, None, 0, ctypes.byref(count),
                              ctypes.byref(grid))
     if st < 0:
         return st, 0, np.zeros((0, WORK_RECORD_INTS), dtype=np.int32)
     rec = np.zeros((max(count.value, 1), WORK_RECORD_INTS), dtype=np.int32)
-    st = lib().bbsa_work_map(B, H, L, d, block, r, dtype, rptr, rec.ctypes.data_as(i32p), count.value,
+    st = lib().bbsa_work_map(B, H, L, d, block, r, dtype, flags, rptr, rec.ctypes.data_as(i32p), count.value,
                              ctypes.byref(count), ctypes.byref(grid))
     return st, grid.value, rec[:count.value]

@@ -68,6 +68,7 @@ constexpr float kPadBias = -10000.0f;
 constexpr float kTau = 8.0f / 1.4426950408889634f;
 constexpr float kTauLog2 = 8.0f;
 constexpr float kInitMax = -1.0e30f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline float group4_max(float x) {
   // Lanes l, l^16, l^32, l^48 hold the same query column.
@@ -162,7 +163,12 @@ __device__ inline void row_sum_f32(const f32x4 (&s)[2][kNT], SoftmaxState &st) {
 // the reference max moves down by the same amount, so it stays the same
 // absolute value (what was accumulated against the old level is rescaled, or
 // vanishes, through the ordinary rescale that follows).
-__device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2], SoftmaxState &st) {
+// With query x key masking each query row scales the key bias (and so the
+// level) by its own mask value mq (the rest of -10000 (1 - m_q m_k) is a
+// per-row constant that cancels in the softmax).
+template <bool QK>
+__device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2], SoftmaxState &st,
+                                  const float (&mq)[kNT]) {
   float bias[2][4];
   float bmax = kInitMax;
 #pragma unroll
@@ -176,7 +182,7 @@ __device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2], Soft
   bmax = group4_max(bmax);
   if (bmax > st.level) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) st.m[nt] += st.level - bmax;
+    for (int nt = 0; nt < kNT; ++nt) st.m[nt] += (QK ? mq[nt] : 1.0f) * (st.level - bmax);
     st.level = bmax;
   }
   bool any = false;
@@ -193,7 +199,7 @@ __device__ inline void apply_mask(f32x4 (&s)[2][kNT], const f32x4 (&mk)[2], Soft
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[mt][nt][i] += bias[mt][i];
+        for (int i = 0; i < 4; ++i) s[mt][nt][i] += QK ? mq[nt] * bias[mt][i] : bias[mt][i];
   }
 }
 
@@ -240,9 +246,9 @@ __device__ inline f32x4 d_run(const f32x4 (&o)[4][kNT], int nt, int i) {
 
 // Finish an item of the fp32 path: either normalise and store the output rows, or store a
 // split-K partial (unnormalised O, reference max, row sum).
-template <typename OutT>
+template <typename OutT, bool RAGGED, bool QK>
 __device__ inline void finish_item(const Params &p, const Item &it, int q0, int nt0, SoftmaxState &st,
-                                   f32x4 (&o)[4][kNT]) {
+                                   f32x4 (&o)[4][kNT], const float (&mq)[kNT]) {
   const int lane = lane_id(), c = lane & 15, g = lane >> 4;
   float lsum[kNT];
 #pragma unroll
@@ -272,8 +278,17 @@ __device__ inline void finish_item(const Params &p, const Item &it, int q0, int 
   OutT *out = (OutT *)p.out + (int64_t)it.bh * p.seq_stride;
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
+    const int qrow = q0 + 16 * (nt0 + nt) + c;
+    if (RAGGED && qrow >= p.L) continue;
+    if (p.lse && g == 0) {
+      // Natural log-sum-exp: the reference (relative to the scaled level),
+      // the level, the log of the row sum, the query x key constant.
+      const float f = QK ? mq[nt] : 1.0f;
+      p.lse[(int64_t)it.bh * p.L + qrow] =
+          st.m[nt] + f * st.level + logf(lsum[nt]) + (QK ? kPadBias * (1.0f - mq[nt]) : 0.0f);
+    }
     const float inv = 1.0f / lsum[nt];
-    OutT *row = out + (int64_t)(q0 + 16 * (nt0 + nt) + c) * kD;
+    OutT *row = out + (int64_t)qrow * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 y = d_run(o, nt, i) * inv;
@@ -339,8 +354,13 @@ constexpr int kWaveLds = 4 * kTileBytes;          // 16 KB per wavefront: K and 
 // the kGroup key chunks of one row tile: those merge their partial results
 // through LDS at the end (one barrier), so a row of up to kGroup chunks
 // needs no separate merge kernel.
-template <bool HAS_MASK>
+template <int MODE>
 __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
+  // MASKING: scores get a padding bias (a mask, or positions past L);
+  // RAGGED: L is not a multiple of the block; QK: query x key masking.
+  constexpr bool MASKING = (MODE & (kModeMask | kModeRagged)) != 0;
+  constexpr bool RAGGED = (MODE & kModeRagged) != 0;
+  constexpr bool QK = (MODE & kModeQK) != 0;
   const int wv = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_workitem_id_x() >> 6);
   const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x(), wv);
   // Idle items only occur as whole groups of full-row items or among middle
@@ -360,7 +380,7 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
   const int b = fdiv(it.bh, p.div_heads);
   const bf16_t *Kbh = (const bf16_t *)p.k + (int64_t)it.bh * p.seq_stride;
   const bf16_t *Vbh = (const bf16_t *)p.v + (int64_t)it.bh * p.seq_stride;
-  const float *mrow = HAS_MASK ? p.mask + (int64_t)b * p.L : nullptr;
+  const float *mrow = (MASKING && p.mask) ? p.mask + (int64_t)b * p.L : nullptr;
   const int q0 = it.qblock * p.block + it.qt * kQT;
 
   // DMA sources inside a 32-key step (elements): instruction u loads key row
@@ -386,15 +406,30 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
     }
   }
 
-  // Q^T operand: lane (c, h) holds Q[q0 + 32nt + c][16k + 8h .. +7].
+  // Q^T operand: lane (c, h) holds Q[q0 + 32nt + c][16k + 8h .. +7] (rows
+  // past L, which exist only with a ragged length, read row L - 1 and are
+  // never stored).
   bf16x8 qf[2][4];
   {
-    const bf16_t *Q = (const bf16_t *)p.q + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
+    const bf16_t *Q = (const bf16_t *)p.q + (int64_t)it.bh * p.seq_stride;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = RAGGED ? min(q0 + 32 * nt + c, p.L - 1) : q0 + 32 * nt + c;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        qf[nt][kk] = *(const bf16x8 *)(Q + (int64_t)(32 * nt + c) * kD + 16 * kk + 8 * h);
+        qf[nt][kk] = *(const bf16x8 *)(Q + (int64_t)row * kD + 16 * kk + 8 * h);
+    }
+  }
+  // Query-side mask value of the lane's two query columns (query x key
+  // masking scales the key bias by it; the rest of -10000 (1 - m_q m_k) is a
+  // per-row constant that cancels in the softmax).
+  float mq[2] = {1.0f, 1.0f};
+  if (QK) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = q0 + 32 * nt + c;
+      mq[nt] = (RAGGED && row >= p.L) ? 0.0f : mrow[row];
+    }
   }
 
   // The plan entries are merged into the walk after the prologue's wait: the
@@ -409,9 +444,9 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
     return __builtin_amdgcn_readlane(walk.blk, i >> lg_spb) * p.block + (i & (walk.steps_per_block - 1)) * kStep;
   };
 
-  // K and V of this (batch, head) as buffer resources: the DMA source of a
-  // lane is a 32-bit per-lane offset plus a scalar offset for the step, and
-  // the hardware range check keeps every read inside the pair's L x d rows.
+  // K and V of this (batch, head) as buffer resources (L x d rows): the DMA
+  // source of a lane is a 32-bit per-lane offset plus a scalar offset for the
+  // step.
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void *)Kbh, (short)0, p.L * kD * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -422,24 +457,41 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) kdma_b[u] = 2 * kdma[u] - 1024 * u;
   const int vdma_b = 2 * vdma;
+  // The hardware range check covers the per-lane offset and the instruction
+  // offset, not the scalar offset.  Every key of an aligned length lies
+  // inside the pair's rows, so the step's row offset rides in the scalar
+  // offset; with a ragged length the last block reaches past L, so there the
+  // row offset joins the per-lane offset and the rows past L read as zeros.
   auto dma_k = [&](int key0, int slot) {
     unsigned char *dst = kbuf + slot * kTileBytes;
-    const int so = key0 * (kD * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[0], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[3], so, 3072, 0);
+    const int so = RAGGED ? 0 : key0 * (kD * 2);
+    const int vo = RAGGED ? key0 * (kD * 2) : 0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[0] + vo, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[1] + vo, so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[2] + vo, so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lptr_t *)dst, 16, kdma_b[3] + vo, so, 3072, 0);
   };
   auto dma_v = [&](int key0, int slot) {
     unsigned char *dst = vbuf + slot * kTileBytes;
-    const int so = key0 * (kD * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vdma_b, so, 3072, 0);
+    const int so = RAGGED ? 0 : key0 * (kD * 2);
+    const int vo = RAGGED ? vdma_b + key0 * (kD * 2) : vdma_b;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vo, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vo, so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vo, so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lptr_t *)dst, 16, vo, so, 3072, 0);
   };
-  // Mask value of key key0 + lane % 32 (one float per lane, lanes l and l + 32 equal).
-  auto load_mask = [&](int key0) -> float { return HAS_MASK ? mrow[key0 + c] : 1.0f; };
+  // Mask value of key key0 + lane % 32 (one float per lane, lanes l and l + 32
+  // equal); positions past L are padding.
+  auto load_mask = [&](int key0) -> float {
+    if constexpr (!MASKING) {
+      return 1.0f;
+    } else if constexpr (RAGGED) {
+      const int key = key0 + c;
+      return key < p.L ? (mrow ? mrow[key] : 1.0f) : 0.0f;
+    } else {
+      return mrow[key0 + c];
+    }
+  };
   auto read_k = [&](int slot, bf16x8 (&kc)[4]) {
     const unsigned char *src = kbuf + slot * kTileBytes;
 #pragma unroll
@@ -482,7 +534,7 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
   // Padding bias for the step whose lane value is mval: nothing when every key
   // is valid, one scalar when all 32 keys share a mask value, per key otherwise.
   auto apply_mask = [&](f32x16 (&sc)[2], float mval) {
-    if (!HAS_MASK) return;
+    if (!MASKING) return;
     const unsigned long long pad = __builtin_amdgcn_ballot_w64(mval != 1.0f);
     if (!pad) return;
     const float m0 = __builtin_amdgcn_readfirstlane(mval);
@@ -490,7 +542,7 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
     if (!__builtin_amdgcn_ballot_w64(mval != m0)) {
       const float bias = bl * (1.0f - m0);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sc[nt] += bias;
+      for (int nt = 0; nt < 2; ++nt) sc[nt] += QK ? bias * mq[nt] : bias;
       return;
     }
     // Per key: register 4j + i holds key 8j + 4h + i, whose mask sits in lane 8j + 4h + i.
@@ -500,8 +552,15 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
       const int key = 8 * (e >> 2) + 4 * h + (e & 3);
       bias[e] = bl * (1.0f - __uint_as_float(__builtin_amdgcn_ds_bpermute(key * 4, __float_as_uint(mval))));
     }
+    if constexpr (QK) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) sc[nt] += bias;
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[nt][e] = __builtin_fmaf(bias[e], mq[nt], sc[nt][e]);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sc[nt] += bias;
+    }
   };
   // p = 2^(s - mref) for query half nt, rounded to bf16 for the PV product; the
   // row sums add the rounded values (the ones the product uses).
@@ -703,14 +762,22 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
       for (int t = 0; t < 4; ++t) acc[t] += w * *(const f32x4 *)(trow + 16 * ((4 * qd + t) ^ (r & 15)));
     }
     if (p.nparts == 1) {
-      const float inv = 1.0f / den;
-      bf16_t *orow = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)(q0 + r) * kD + 16 * qd;
-      const bf16x8 v0 = __builtin_shufflevector(__builtin_convertvector(acc[0] * inv, bf16x4),
-                                                __builtin_convertvector(acc[1] * inv, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 v1 = __builtin_shufflevector(__builtin_convertvector(acc[2] * inv, bf16x4),
-                                                __builtin_convertvector(acc[3] * inv, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
-      __builtin_nontemporal_store(v0, (bf16x8 *)orow);
-      __builtin_nontemporal_store(v1, (bf16x8 *)(orow + 8));
+      if (!RAGGED || q0 + r < p.L) {
+        const float inv = 1.0f / den;
+        bf16_t *orow = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)(q0 + r) * kD + 16 * qd;
+        const bf16x8 v0 = __builtin_shufflevector(__builtin_convertvector(acc[0] * inv, bf16x4),
+                                                  __builtin_convertvector(acc[1] * inv, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 v1 = __builtin_shufflevector(__builtin_convertvector(acc[2] * inv, bf16x4),
+                                                  __builtin_convertvector(acc[3] * inv, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+        __builtin_nontemporal_store(v0, (bf16x8 *)orow);
+        __builtin_nontemporal_store(v1, (bf16x8 *)(orow + 8));
+        if (p.lse && qd == 0) {
+          // Natural log-sum-exp of the row: (M + log2 den) / log2(e), plus the
+          // query x key constant -10000 (1 - m_q).
+          const float cq = QK ? kPadBias * (1.0f - mrow[q0 + r]) : 0.0f;
+          p.lse[(int64_t)it.bh * p.L + q0 + r] = (M + log2f(den)) * kLn2 + cq;
+        }
+      }
     } else {
       // A partial over this group of chunks for the merge kernel (bias
       // level 0: the bf16 scores carry the whole padding bias).
@@ -744,6 +811,17 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
         }
     }
   }
+  if (p.lse && h == 0) {
+    // Natural log-sum-exp of each row: (mref + log2 l) / log2(e), plus the
+    // query x key constant -10000 (1 - m_q).
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = q0 + 32 * nt + c;
+      if (!RAGGED || row < p.L)
+        p.lse[(int64_t)it.bh * p.L + row] = (mref[nt] + log2f(lsum[nt])) * kLn2 +
+                                            (QK ? kPadBias * (1.0f - mq[nt]) : 0.0f);
+    }
+  }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in this wavefront's own LDS region
   {
     bf16_t *out = (bf16_t *)p.out + (int64_t)it.bh * p.seq_stride + (int64_t)q0 * kD;
@@ -752,7 +830,8 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
     for (int i = 0; i < 8; ++i) {
       const int q = 8 * i + (lane >> 3);
       const bf16x8 v = *(const bf16x8 *)(kbuf + q * 128 + 16 * (ch ^ (q & 7)));
-      __builtin_nontemporal_store(v, (bf16x8 *)(out + (int64_t)q * kD + 8 * ch));   // never re-read here
+      if (!RAGGED || q0 + q < p.L)
+        __builtin_nontemporal_store(v, (bf16x8 *)(out + (int64_t)q * kD + 8 * ch));   // never re-read here
     }
   }
 }
@@ -765,8 +844,11 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
 // uses the order d = 16g + s (s = MFMA step) on both operands; the PV
 // contraction steps over (mt, i) with key 16mt + 4g + i, read straight from
 // memory.
-template <bool HAS_MASK>
+template <int MODE>
 __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
+  constexpr bool MASKING = (MODE & (kModeMask | kModeRagged)) != 0;
+  constexpr bool RAGGED = (MODE & kModeRagged) != 0;
+  constexpr bool QK = (MODE & kModeQK) != 0;
   const Item it = decode_item(p, (int)__builtin_amdgcn_workgroup_id_x(), 0);
   if (it.bh >= p.bh_total) return;
   // The kF32Waves wavefronts of a workgroup split the item's 64 query rows:
@@ -777,24 +859,30 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
   const float *Q = (const float *)p.q + (int64_t)it.bh * p.seq_stride;
   const float *K = (const float *)p.k + (int64_t)it.bh * p.seq_stride;
   const float *V = (const float *)p.v + (int64_t)it.bh * p.seq_stride;
-  const float *mrow = HAS_MASK ? p.mask + (int64_t)b * p.L : nullptr;
+  const float *mrow = (MASKING && p.mask) ? p.mask + (int64_t)b * p.L : nullptr;
   const int q0 = it.qblock * p.block + it.qt * kQT;
 
+  // Query rows past L (a ragged length) read row L - 1 and are never stored.
   float qf[kNT][16];
+  float mq[kNT];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int row = q0 + 16 * (nt0 + nt) + c;
+    const int lrow = RAGGED ? min(row, p.L - 1) : row;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const f32x4 x = *(const f32x4 *)(Q + (int64_t)(q0 + 16 * (nt0 + nt) + c) * kD + 16 * g + 4 * s4);
+      const f32x4 x = *(const f32x4 *)(Q + (int64_t)lrow * kD + 16 * g + 4 * s4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf[nt][4 * s4 + e] = x[e];
     }
+    mq[nt] = QK ? ((RAGGED && row >= p.L) ? 0.0f : mrow[row]) : 1.0f;
+  }
 
   const KeyWalk walk = make_walk(p, it);
   SoftmaxState st;
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) { st.m[nt] = kInitMax; st.l[nt] = 0.0f; }
-  st.level = HAS_MASK ? kInitMax : 0.0f;
+  st.level = MASKING ? kInitMax : 0.0f;
   f32x4 o[4][kNT];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -810,23 +898,37 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
     float va[2][4][4];
     f32x4 mc[2];
   };
+  // With a ragged length, key rows past L read as zeros (and count as padding).
   auto load_step = [&](int key0, StepOperands &x) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+      const int kr = key0 + 16 * mt + c;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const f32x4 v4 = *(const f32x4 *)(K + (int64_t)(key0 + 16 * mt + c) * kD + 16 * g + 4 * s4);
+        f32x4 v4 = *(const f32x4 *)(K + (int64_t)(RAGGED ? min(kr, p.L - 1) : kr) * kD + 16 * g + 4 * s4);
+        if (RAGGED && kr >= p.L) v4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; ++e) x.kf[mt][4 * s4 + e] = v4[e];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 v4 = *(const f32x4 *)(V + (int64_t)(key0 + 16 * mt + 4 * g + i) * kD + 4 * c);
+        const int vr = key0 + 16 * mt + 4 * g + i;
+        f32x4 v4 = *(const f32x4 *)(V + (int64_t)(RAGGED ? min(vr, p.L - 1) : vr) * kD + 4 * c);
+        if (RAGGED && vr >= p.L) v4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) x.va[mt][i][dt] = v4[dt];
       }
     }
-    if (HAS_MASK) {
+    if constexpr (RAGGED) {
+      // Element loads: the mask row of a ragged length is not 16-byte aligned.
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = key0 + 16 * mt + 4 * g + e;
+          x.mc[mt][e] = key < p.L ? (mrow ? mrow[key] : 1.0f) : 0.0f;
+        }
+    } else if constexpr (MASKING) {
       x.mc[0] = *(const f32x4 *)(mrow + key0 + 4 * g);
       x.mc[1] = *(const f32x4 *)(mrow + key0 + 16 + 4 * g);
     }
@@ -860,9 +962,9 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.kf[mt][ks], qf[nt][ks], acc, 0, 0, 0);
         s[mt][nt] = acc;
       }
-    if (HAS_MASK) {
+    if (MASKING) {
       f32x4 mc[2] = {x.mc[0], x.mc[1]};
-      apply_mask(s, mc, st);
+      apply_mask<QK>(s, mc, st, mq);
     }
     softmax_rescale(s, st, o);
     softmax_exp(s, st);
@@ -877,7 +979,7 @@ __global__ __launch_bounds__(64 * kF32Waves) void bbsa_attn_f32(Params p) {
           for (int nt = 0; nt < kNT; ++nt)
             o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.va[mt][i][dt], s[mt][nt][i], o[dt][nt], 0, 0, 0);
   }
-  finish_item<float>(p, it, q0, nt0, st, o);
+  finish_item<float, RAGGED, QK>(p, it, q0, nt0, st, o, mq);
 }
 
 // ---------------------------------------------------------------- split-K merge
@@ -905,8 +1007,15 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   const float *base = p.ws + first * kPartialFloats;
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int q = 4 * slice + (tid >> 4), dq = tid & 15;
+  const int qblock = full_row ? ((p.n_rows_global == 2) ? (row == 0 ? 0 : p.nb - 1) : row) : 1 + i_mid;
+  const int qrow = qblock * p.block + qt * kQT + q;
+  if ((p.mode & kModeRagged) && qrow >= p.L) return;   // a row past a ragged length: nothing to write
+  // Query x key masking scales each row's bias, and so its levels, by the
+  // row's mask value.
+  const bool qk = (p.mode & kModeQK) != 0;
+  const float mq = qk ? p.mask[(int64_t)fdiv(bh, p.div_heads) * p.L + qrow] : 1.0f;
   // Each partial's maxima are relative to its padding-bias level: partial c
-  // enters with exponent m_c + (level_c - top level) * log2(e), where the
+  // enters with exponent m_c + mq (level_c - top level) * log2(e), where the
   // level difference is exact for 0/1 masks (and 0 on the bf16 path).
   float top = kInitMax;
   for (int ch = 0; ch < np; ++ch) top = __builtin_fmaxf(top, base[(int64_t)ch * kPartialFloats + kQT * kD + 2 * kQT]);
@@ -922,7 +1031,7 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
     for (int u = 0; u < kMergeBatch; ++u) {
       const int ch = min(c0 + u, np - 1);   // repeats stay unused
       const float *part = base + (int64_t)ch * kPartialFloats;
-      mc[u] = part[kQT * kD + q] + (part[kQT * kD + 2 * kQT] - top) * kLog2e;
+      mc[u] = part[kQT * kD + q] + mq * (part[kQT * kD + 2 * kQT] - top) * kLog2e;
       lc[u] = part[kQT * kD + kQT + q];
       oc[u] = *(const f32x4 *)(part + q * kD + 4 * dq);
     }
@@ -942,8 +1051,10 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
     M = Mb;
   }
   const f32x4 y = acc * (1.0f / den);
-  const int qblock = full_row ? ((p.n_rows_global == 2) ? (row == 0 ? 0 : p.nb - 1) : row) : 1 + i_mid;
-  OutT *dst = (OutT *)p.out + (int64_t)bh * p.seq_stride + (int64_t)(qblock * p.block + qt * kQT + q) * kD + 4 * dq;
+  if (p.lse && dq == 0)
+    p.lse[(int64_t)bh * p.L + qrow] =
+        (M + log2f(den)) * kLn2 + mq * top + (qk ? kPadBias * (1.0f - mq) : 0.0f);
+  OutT *dst = (OutT *)p.out + (int64_t)bh * p.seq_stride + (int64_t)qrow * kD + 4 * dq;
   if constexpr (sizeof(OutT) == 2) {
     *(bf16x4 *)dst = __builtin_convertvector(y, bf16x4);
   } else {
@@ -1002,7 +1113,7 @@ int ensure_workspace(size_t bytes, hipStream_t stream, float **ws) {
 }
 
 // Enqueue the kernels of a validated call (its workspace pointer set).
-int launch_forward(const Launch &ln, const float *mask, hipStream_t stream, bbsa_dtype dtype, int status) {
+int launch_forward(const Launch &ln, hipStream_t stream, bbsa_dtype dtype, int status) {
   const Params &p = ln.p;
   std::unique_lock<std::mutex> tlock(g_timing.mu);
   const bool timed = g_timing.enabled && g_timing.n < kMaxTimed;
@@ -1015,12 +1126,28 @@ int launch_forward(const Launch &ln, const float *mask, hipStream_t stream, bbsa
   }
   if (timed && hipEventRecord(g_timing.ev[tslot][0], stream) != hipSuccess) return BBSA_ERR_HIP;
   const dim3 g1((unsigned)ln.grid), b1((unsigned)ln.block_threads);
-  if (dtype == BBSA_BF16) {
-    if (mask) hipLaunchKernelGGL(bbsa_attn_bf16<true>, g1, b1, 0, stream, p);
-    else hipLaunchKernelGGL(bbsa_attn_bf16<false>, g1, b1, 0, stream, p);
-  } else {
-    if (mask) hipLaunchKernelGGL(bbsa_attn_f32<true>, g1, b1, 0, stream, p);
-    else hipLaunchKernelGGL(bbsa_attn_f32<false>, g1, b1, 0, stream, p);
+  switch (p.mode | (dtype == BBSA_BF16 ? 0 : 8)) {
+    case 0: hipLaunchKernelGGL(bbsa_attn_bf16<0>, g1, b1, 0, stream, p); break;
+    case kModeMask: hipLaunchKernelGGL(bbsa_attn_bf16<kModeMask>, g1, b1, 0, stream, p); break;
+    case kModeRagged: hipLaunchKernelGGL(bbsa_attn_bf16<kModeRagged>, g1, b1, 0, stream, p); break;
+    case kModeMask | kModeRagged:
+      hipLaunchKernelGGL(bbsa_attn_bf16<kModeMask | kModeRagged>, g1, b1, 0, stream, p);
+      break;
+    case kModeMask | kModeQK: hipLaunchKernelGGL(bbsa_attn_bf16<kModeMask | kModeQK>, g1, b1, 0, stream, p); break;
+    case kModeMask | kModeRagged | kModeQK:
+      hipLaunchKernelGGL(bbsa_attn_bf16<kModeMask | kModeRagged | kModeQK>, g1, b1, 0, stream, p);
+      break;
+    case 8: hipLaunchKernelGGL(bbsa_attn_f32<0>, g1, b1, 0, stream, p); break;
+    case 8 | kModeMask: hipLaunchKernelGGL(bbsa_attn_f32<kModeMask>, g1, b1, 0, stream, p); break;
+    case 8 | kModeRagged: hipLaunchKernelGGL(bbsa_attn_f32<kModeRagged>, g1, b1, 0, stream, p); break;
+    case 8 | kModeMask | kModeRagged:
+      hipLaunchKernelGGL(bbsa_attn_f32<kModeMask | kModeRagged>, g1, b1, 0, stream, p);
+      break;
+    case 8 | kModeMask | kModeQK: hipLaunchKernelGGL(bbsa_attn_f32<kModeMask | kModeQK>, g1, b1, 0, stream, p); break;
+    case 8 | kModeMask | kModeRagged | kModeQK:
+      hipLaunchKernelGGL(bbsa_attn_f32<kModeMask | kModeRagged | kModeQK>, g1, b1, 0, stream, p);
+      break;
+    default: return BBSA_ERR_ARG;
   }
   if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
   if (timed && hipEventRecord(g_timing.ev[tslot][1], stream) != hipSuccess) return BBSA_ERR_HIP;
@@ -1078,7 +1205,21 @@ extern "C" int bbsa_forward(const void *q, const void *k, const void *v, const f
     const int rc = ensure_workspace((size_t)ln.n_partials * kPartialFloats * sizeof(float), stream, &ln.p.ws);
     if (rc != BBSA_OK) return rc;
   }
-  return launch_forward(ln, mask, stream, dtype, st);
+  return launch_forward(ln, stream, dtype, st);
+}
+
+extern "C" int bbsa_forward_ex(const void *q, const void *k, const void *v, const float *mask,
+                               const int32_t *rand_attn, int B, int H, int L, int d, int block, int r, void *out,
+                               float *lse, hipStream_t stream, bbsa_dtype dtype, unsigned flags) {
+  Launch ln;
+  const int st =
+      setup_forward_ex(q, k, v, mask, rand_attn, B, H, L, d, block, r, out, lse, (int)dtype, flags, &ln);
+  if (st < 0) return st;
+  if (ln.n_partials > 0) {
+    const int rc = ensure_workspace((size_t)ln.n_partials * kPartialFloats * sizeof(float), stream, &ln.p.ws);
+    if (rc != BBSA_OK) return rc;
+  }
+  return launch_forward(ln, stream, dtype, st);
 }
 
 extern "C" int bbsa_forward_noalloc(const void *q, const void *k, const void *v, const float *mask,
@@ -1092,7 +1233,7 @@ extern "C" int bbsa_forward_noalloc(const void *q, const void *k, const void *v,
     const int rc = scratch_address(&ln.p.ws);
     if (rc != BBSA_OK) return rc;
   }
-  return launch_forward(ln, mask, stream, dtype, st);
+  return launch_forward(ln, stream, dtype, st);
 }
 
 extern "C" const char *bbsa_status_string(int status) {

@@ -11,15 +11,15 @@
 
 using namespace bbsa_sched;
 
-extern "C" int bbsa_work_map(int B, int H, int L, int d, int block, int r, bbsa_dtype dtype,
+extern "C" int bbsa_work_map(int B, int H, int L, int d, int block, int r, bbsa_dtype dtype, unsigned flags,
                              const int32_t *rand_attn, int32_t *records, int64_t capacity,
                              int64_t *count, int64_t *grid) {
   if (!count || !grid) return BBSA_ERR_ARG;
   // Stand-in device addresses: only their alignment is looked at.
   void *const fake = (void *)(uintptr_t)4096;
   Launch ln;
-  const int st = setup_forward(fake, fake, fake, nullptr, rand_attn, B, H, L, d, block, r, fake,
-                               (int)dtype, &ln);
+  const int st = setup_forward_ex(fake, fake, fake, nullptr, rand_attn, B, H, L, d, block, r, fake, nullptr,
+                                  (int)dtype, flags, &ln);
   if (st < 0) return st;
   const Params &p = ln.p;
   const int waves = (dtype == BBSA_BF16) ? p.group : 1;

@@ -65,14 +65,21 @@ __host__ __device__ inline int fdiv(int n, const FastDiv &f) {
   return (int)((hi + (uint32_t)n) >> f.s);
 }
 
+// Kernel variants (template argument of the attention kernels).
+constexpr int kModeMask = 1;     // a padding mask is given
+constexpr int kModeRagged = 2;   // L is not a multiple of the block: positions L .. nb * block - 1 are padding
+constexpr int kModeQK = 4;       // query x key masking: bias -10000 (1 - m[query] m[key])
+
 struct Params {
   const void *q, *k, *v;
   const float *mask;         // [B, L] or null
   const int32_t *rand_attn;  // [H, nb-2, r]
   void *out;
+  float *lse;                // [B, H, L] row log-sum-exp, or null
   float *ws;                 // split-K partials
   int64_t seq_stride;        // L * d elements per (batch, head)
-  int B, H, L, nb, block, r;
+  int B, H, L, nb, block, r; // L: the real length; nb = ceil(L / block)
+  int mode;                  // kMode* bits of the launched kernels
   int qtiles;                // block / 64: 64-row query tiles per query block
   int n_rows_global;         // query blocks handled as full rows: 2, or nb on the fallback
   int chunks;                // key chunks per full row (block range [c nb / chunks, (c + 1) nb / chunks))
@@ -205,22 +212,29 @@ struct Launch {
   bool full;            // short-sequence fallback: full attention
 };
 
-// Validate a forward call and size its launch.  Returns BBSA_OK,
+// Validate a forward call and size its launch.  flags: BBSA_FLAG_* (a
+// length that is not a multiple of the block needs BBSA_FLAG_PAD_TO_BLOCK);
+// lse: optional row log-sum-exp output.  Returns BBSA_OK,
 // BBSA_OK_FULL_FALLBACK or a negative status; no HIP call is made.
-inline int setup_forward(const void *q, const void *k, const void *v, const float *mask,
-                         const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
-                         void *out, int dtype, Launch *launch) {
+inline int setup_forward_ex(const void *q, const void *k, const void *v, const float *mask,
+                            const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
+                            void *out, float *lse, int dtype, unsigned flags, Launch *launch) {
   if (!q || !k || !v || !out || !launch) return BBSA_ERR_ARG;
+  if (flags & ~(unsigned)(BBSA_FLAG_PAD_TO_BLOCK | BBSA_FLAG_QUERY_KEY_MASK)) return BBSA_ERR_ARG;
   // The kernels move q, k, v, out and the mask in 16-byte pieces.
   auto misaligned = [](const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
-      (mask && misaligned(mask, 16)) || (rand_attn && misaligned(rand_attn, 4)))
+      (mask && misaligned(mask, 16)) || (rand_attn && misaligned(rand_attn, 4)) || (lse && misaligned(lse, 4)))
     return BBSA_ERR_ARG;
   if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block <= 0 || r < 1) return BBSA_ERR_ARG;
   if (dtype != BBSA_BF16 && dtype != BBSA_F32) return BBSA_ERR_UNSUPPORTED;
   if (d != kD || (block != 64 && block != 128)) return BBSA_ERR_UNSUPPORTED;
-  if (L % block != 0) return BBSA_ERR_SHAPE;
-  const int nb = L / block;
+  const bool ragged = L % block != 0;
+  if (ragged && !(flags & BBSA_FLAG_PAD_TO_BLOCK)) return BBSA_ERR_SHAPE;
+  if (L > kMaxL) return BBSA_ERR_UNSUPPORTED;
+  const int nb = L / block + (ragged ? 1 : 0);
+  // The fallback test on the padded length: (5 + 2r) * block is a multiple
+  // of the block, so it is the same test on L.
   const bool full = (int64_t)L <= (int64_t)(5 + 2 * (int64_t)r) * block;
   if (!full) {
     if (!rand_attn) return BBSA_ERR_ARG;
@@ -231,13 +245,14 @@ inline int setup_forward(const void *q, const void *k, const void *v, const floa
   // one (batch, head)'s K or V rows must fit a 32-bit byte range (the bf16
   // kernel addresses them through a buffer resource): L <= 2^24.
   const int64_t bh = (int64_t)B * H;
-  if (bh > 0x7fffffff || (int64_t)B * H * L * kD > ((int64_t)1 << 40)) return BBSA_ERR_UNSUPPORTED;
-  if (L > kMaxL) return BBSA_ERR_UNSUPPORTED;
+  if (bh > 0x7fffffff || (int64_t)B * H * nb * block * kD > ((int64_t)1 << 40)) return BBSA_ERR_UNSUPPORTED;
 
   Params p{};
-  p.q = q; p.k = k; p.v = v; p.mask = mask; p.rand_attn = rand_attn; p.out = out;
+  p.q = q; p.k = k; p.v = v; p.mask = mask; p.rand_attn = rand_attn; p.out = out; p.lse = lse;
   p.seq_stride = (int64_t)L * kD;
   p.B = B; p.H = H; p.L = L; p.nb = nb; p.block = block; p.r = r;
+  p.mode = (mask ? kModeMask : 0) | (ragged ? kModeRagged : 0) |
+           ((mask && (flags & BBSA_FLAG_QUERY_KEY_MASK)) ? kModeQK : 0);
   p.qtiles = block / kQT;
   p.n_rows_global = full ? nb : 2;
   // Full rows are cut into chunks of about 1024 keys (bf16) or 256 keys (the
@@ -297,6 +312,12 @@ inline int setup_forward(const void *q, const void *k, const void *v, const floa
   launch->n_partials = n_part_full + n_part_mid;
   launch->full = full;
   return full ? BBSA_OK_FULL_FALLBACK : BBSA_OK;
+}
+
+inline int setup_forward(const void *q, const void *k, const void *v, const float *mask,
+                         const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
+                         void *out, int dtype, Launch *launch) {
+  return setup_forward_ex(q, k, v, mask, rand_attn, B, H, L, d, block, r, out, nullptr, dtype, 0u, launch);
 }
 
 }  // namespace bbsa_sched

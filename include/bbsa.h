@@ -36,6 +36,12 @@ extern "C" {
 /* Element type of q, k, v and out. */
 typedef enum { BBSA_BF16 = 0, BBSA_F32 = 1 } bbsa_dtype;
 
+/* Options of bbsa_forward_ex (bit flags). */
+enum {
+  BBSA_FLAG_PAD_TO_BLOCK = 1,   /* L need not be a multiple of the block */
+  BBSA_FLAG_QUERY_KEY_MASK = 2  /* bias -10000 (1 - mask[query] mask[key]) */
+};
+
 /* Status codes. */
 enum {
   BBSA_OK = 0,               /* success */
@@ -180,6 +186,42 @@ int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
                  void *out, hipStream_t stream, bbsa_dtype dtype);
 
 /*
+ * bbsa_forward with options, and the row log-sum-exp.
+ *
+ * flags (bit OR of):
+ *   BBSA_FLAG_PAD_TO_BLOCK: L need not be a multiple of `block`.  [BP]
+ *     section "序列长度的块对齐要求": the encoder pads its input to a
+ *     multiple of the block size and cuts the padding off its output.  The
+ *     call behaves as if q, k, v were extended with zero rows and the mask
+ *     with zeros up to nb = ceil(L / block) blocks, then trimmed: positions
+ *     L .. nb*block-1 are never read or written (the kernels treat them as
+ *     padded keys with zero K and V), rand_attn is the plan of nb blocks
+ *     ([H, nb-2, r]) and the fallback test is L <= (5 + 2r) * block.  The
+ *     tensors keep their [B, H, L, d] / [B, L] layout with the real L.
+ *   BBSA_FLAG_QUERY_KEY_MASK: the bias of query t and key u is
+ *     -10000 * (1 - mask[b, t] * mask[b, u]), the outer product of the query
+ *     and key masks that [BB] section "随机块掩码是如何生成的" builds the band
+ *     mask from (BigBirdMasks' einsum), instead of the key-side
+ *     -10000 * (1 - mask[b, u]).  Rows of valid queries are unchanged; a
+ *     padded query row gets the same bias on every key, i.e. a softmax of
+ *     its raw scores.  No effect without a mask.
+ * lse: device float32 [B, H, L], 4-byte aligned, caller-owned, or NULL: the
+ *     natural log-sum-exp of each query row's scores (bias included) over
+ *     the keys it attends, the quantity a recompute-based backward needs.
+ *     On the bf16 path the row sums add the bf16-rounded probabilities, so
+ *     lse carries a relative error of up to 2^-9 in the sum (about 2e-3 in
+ *     lse); on the fp32 path it is exact to fp32 rounding of its terms.
+ *
+ * Other arguments, limits, workspace use and errors as bbsa_forward; an
+ * unknown flag bit is BBSA_ERR_ARG, a length that is not a multiple of the
+ * block without BBSA_FLAG_PAD_TO_BLOCK is BBSA_ERR_SHAPE.  With flags 0 and
+ * lse NULL the call is exactly bbsa_forward.
+ */
+int bbsa_forward_ex(const void *q, const void *k, const void *v, const float *mask,
+                    const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
+                    void *out, float *lse, hipStream_t stream, bbsa_dtype dtype, unsigned flags);
+
+/*
  * bbsa_forward for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  *
@@ -227,7 +269,8 @@ int bbsa_timing_read(double *main_ms, double *combine_ms, int *calls);
 
 /*
  * Work decomposition of a forward call (a query for tests and tools; no HIP
- * call).  For the shape and dtype of a bbsa_forward call with host plan
+ * call).  For the shape, dtype and flags of a bbsa_forward_ex call (flags 0:
+ * a bbsa_forward call) with host plan
  * `rand_attn` (may be NULL on the fallback), runs on the host the same item
  * mapping and key-list construction the kernels run, and writes one record
  * of BBSA_WORK_RECORD_INTS int32 per work item (a 64-row query tile against
@@ -246,7 +289,7 @@ int bbsa_timing_read(double *main_ms, double *combine_ms, int *calls);
  * what bbsa_forward would return for the shape (pointer arguments aside).
  */
 #define BBSA_WORK_RECORD_INTS 80
-int bbsa_work_map(int B, int H, int L, int d, int block, int r, bbsa_dtype dtype,
+int bbsa_work_map(int B, int H, int L, int d, int block, int r, bbsa_dtype dtype, unsigned flags,
                   const int32_t *rand_attn, int32_t *records, int64_t capacity,
                   int64_t *count, int64_t *grid);
 

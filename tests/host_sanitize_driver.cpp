@@ -90,6 +90,24 @@ static void validation() {
                    c.block, c.r, c.dtype, st, c.want);
     CHECK(st == c.want);
   }
+  // bbsa_forward_ex: flags, ragged lengths, lse alignment.
+  float *const lse = (float *)(uintptr_t)4096;
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, 1000, 64, 64, 3, P, lse, 0, 0u, &ln) == BBSA_ERR_SHAPE);
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, 1000, 64, 64, 3, P, lse, 0, 1u, &ln) == BBSA_OK);
+  CHECK(ln.p.nb == 16 && ln.p.L == 1000 && (ln.p.mode & kModeRagged));
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, 1000, 64, 64, 3, P, lse, 0, 8u, &ln) == BBSA_ERR_ARG);
+  CHECK(setup_forward_ex(P, P, P, (const float *)P, ra, 1, 1, 1024, 64, 64, 3, P, lse, 0, 2u, &ln) == BBSA_OK);
+  CHECK(ln.p.mode == (kModeMask | kModeQK));
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, 1024, 64, 64, 3, P, lse, 0, 2u, &ln) == BBSA_OK);
+  CHECK(ln.p.mode == 0);   // query x key masking without a mask: nothing to do
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, 1024, 64, 64, 3, P, (float *)(uintptr_t)4098, 0, 0u, &ln) ==
+        BBSA_ERR_ARG);
+  CHECK(setup_forward_ex(P, P, P, nullptr, nullptr, 1, 1, 700, 64, 64, 3, P, nullptr, 0, 1u, &ln) ==
+        BBSA_OK_FULL_FALLBACK);
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, (1 << 24) - 1, 64, 64, 3, P, nullptr, 0, 1u, &ln) ==
+        BBSA_ERR_UNSUPPORTED);   // chunks * nb >= 2^31
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, (1 << 24) + 1, 64, 64, 3, P, nullptr, 0, 1u, &ln) ==
+        BBSA_ERR_UNSUPPORTED);   // L > 2^24
   // Null and misaligned pointers.
   void *const M = (void *)(uintptr_t)4104;
   CHECK(setup_forward(nullptr, P, P, nullptr, ra, 1, 1, 1024, 64, 64, 3, P, 0, &ln) == BBSA_ERR_ARG);
@@ -128,16 +146,16 @@ static void work_maps() {
     const bool full = s.L <= (5 + 2 * s.r) * s.block;
     if (!full) CHECK(bbsa_plan_rand_attn(plan.data(), s.H, nb, s.r, 11) == BBSA_OK);
     int64_t count = 0, grid = 0;
-    int st = bbsa_work_map(s.B, s.H, s.L, 64, s.block, s.r, (bbsa_dtype)s.dtype, full ? nullptr : plan.data(),
+    int st = bbsa_work_map(s.B, s.H, s.L, 64, s.block, s.r, (bbsa_dtype)s.dtype, 0u, full ? nullptr : plan.data(),
                            nullptr, 0, &count, &grid);
     CHECK(st >= 0 && count > 0 && grid > 0);
     std::vector<int32_t> rec((size_t)count * BBSA_WORK_RECORD_INTS);
     // A buffer one record short: the query must not write past it.
     int64_t count2 = 0, grid2 = 0;
-    st = bbsa_work_map(s.B, s.H, s.L, 64, s.block, s.r, (bbsa_dtype)s.dtype, full ? nullptr : plan.data(),
+    st = bbsa_work_map(s.B, s.H, s.L, 64, s.block, s.r, (bbsa_dtype)s.dtype, 0u, full ? nullptr : plan.data(),
                        rec.data(), count - 1, &count2, &grid2);
     CHECK(st >= 0 && count2 == count && grid2 == grid);
-    st = bbsa_work_map(s.B, s.H, s.L, 64, s.block, s.r, (bbsa_dtype)s.dtype, full ? nullptr : plan.data(),
+    st = bbsa_work_map(s.B, s.H, s.L, 64, s.block, s.r, (bbsa_dtype)s.dtype, 0u, full ? nullptr : plan.data(),
                        rec.data(), count, &count2, &grid2);
     CHECK(st >= 0);
     for (int64_t i = 0; i < count; ++i) {
@@ -147,8 +165,8 @@ static void work_maps() {
     }
   }
   int64_t c = 0, g = 0;
-  CHECK(bbsa_work_map(1, 1, 1024, 64, 64, 3, BBSA_BF16, nullptr, nullptr, 0, nullptr, &g) == BBSA_ERR_ARG);
-  CHECK(bbsa_work_map(1, 1, 1024, 64, 64, 3, BBSA_BF16, nullptr, nullptr, 0, &c, &g) == BBSA_ERR_ARG);
+  CHECK(bbsa_work_map(1, 1, 1024, 64, 64, 3, BBSA_BF16, 0u, nullptr, nullptr, 0, nullptr, &g) == BBSA_ERR_ARG);
+  CHECK(bbsa_work_map(1, 1, 1024, 64, 64, 3, BBSA_BF16, 0u, nullptr, nullptr, 0, &c, &g) == BBSA_ERR_ARG);
 }
 
 int main() {

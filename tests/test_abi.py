@@ -86,3 +86,14 @@ def test_noalloc_validates_like_forward(lib):
         assert st == code
     st = lib.bbsa_forward_noalloc(FAKE, FAKE, FAKE, None, FAKE, 8, 16, 32768, 64, 64, 3, FAKE, None, 0)
     assert st == bbsa.BBSA_ERR_SCRATCH
+
+
+def test_forward_ex_validates(lib):
+    # Unknown flag bits, a ragged length without the padding flag, and the
+    # usual argument errors; no HIP call happens for any of them.
+    def ex(L=1024, flags=0, lse=None, q=FAKE):
+        return lib.bbsa_forward_ex(q, FAKE, FAKE, None, FAKE, 1, 1, L, 64, 64, 3, FAKE, lse, None, 0, flags)
+    assert ex(flags=4) == bbsa.BBSA_ERR_ARG
+    assert ex(L=1000) == bbsa.BBSA_ERR_SHAPE
+    assert ex(q=None) == bbsa.BBSA_ERR_ARG
+    assert ex(L=1000, flags=1, lse=ctypes.c_void_p(0x1002)) == bbsa.BBSA_ERR_ARG   # lse 4-byte aligned

@@ -51,11 +51,11 @@ SHAPES = [
 ]
 
 
-def _check(B, H, L, block, r, dtype):
-    nb = L // block
+def _check(B, H, L, block, r, dtype, flags=0):
+    nb = -(-L // block)
     full = L <= (5 + 2 * r) * block
     plan = None if full else oracle.plan_rand_attn(H, nb, r, 3)
-    st, grid, rec = bbsa.bbsa_work_map(B, H, L, 64, block, r, dtype, plan)
+    st, grid, rec = bbsa.bbsa_work_map(B, H, L, 64, block, r, dtype, plan, flags=flags)
     assert st == (bbsa.BBSA_OK_FULL_FALLBACK if full else bbsa.BBSA_OK)
     qtiles = block // 64
     waves = 4 if dtype == bbsa.BBSA_BF16 else 1
@@ -105,6 +105,21 @@ def _check(B, H, L, block, r, dtype):
 @pytest.mark.parametrize("B,H,L,block,r,dtype", SHAPES)
 def test_work_map_covers_the_pattern_once(lib, B, H, L, block, r, dtype):
     _check(B, H, L, block, r, dtype)
+
+
+@pytest.mark.parametrize("B,H,L,block,r,dtype", [
+    (4, 12, 4000, 64, 3, bbsa.BBSA_BF16),    # ragged: 63 blocks, the last one partial
+    (1, 3, 5000, 128, 2, bbsa.BBSA_BF16),
+    (2, 2, 1000, 64, 3, bbsa.BBSA_F32),
+    (1, 2, 700, 64, 3, bbsa.BBSA_BF16),      # ragged and short: fallback
+    (1, 1, 16385, 64, 3, bbsa.BBSA_BF16),    # one token past a block boundary
+])
+def test_work_map_ragged_lengths(lib, B, H, L, block, r, dtype):
+    # Lengths that are not a multiple of the block (padded to the block):
+    # the pattern of ceil(L / block) blocks is covered exactly once.
+    _check(B, H, L, block, r, dtype, flags=bbsa.BBSA_FLAG_PAD_TO_BLOCK)
+    # Without the flag such a length is refused.
+    assert bbsa.bbsa_work_map(B, H, L, 64, block, r, dtype, None)[0] == bbsa.BBSA_ERR_SHAPE
 
 
 def test_work_map_reports_errors_like_forward(lib):
