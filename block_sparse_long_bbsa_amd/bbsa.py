@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.bbsa_forward_ex.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + \
             [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint]
         L.bbsa_forward_ex.restype = ctypes.c_int
+        L.bbsa_attention_probs.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 6 + \
+            [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint]
+        L.bbsa_attention_probs.restype = ctypes.c_int
         L.bbsa_status_string.argtypes = [ctypes.c_int]
         L.bbsa_status_string.restype = ctypes.c_char_p
         L.bbsa_release_workspace.argtypes = []
@@ -253,6 +256,27 @@ def bbsa_forward_ex(q, k, v, mask, rand_attn, block: int, r: int, out=None, lse=
         st = lib().bbsa_forward_ex(*cargs)
     _status(st, "bbsa_forward_ex", L, block, r, warn_fallback)
     return (out, lse, st) if lse is not None else (out, st)
+
+
+def bbsa_attention_probs(q, k, mask, rand_attn, block: int, r: int, probs=None, stream=None,
+                         pad_to_block: bool = False, query_key_mask: bool = False):
+    """Dense float32 ``[B, H, L, L]`` attention probabilities of the pattern
+    (zeros outside it); see include/bbsa.h.  Returns ``(probs, status)``."""
+    import torch
+    B, H, L, d = q.shape
+    if probs is None:
+        probs = torch.empty((B, H, L, L), dtype=torch.float32, device=q.device)
+    if not probs.is_cuda or probs.dtype != torch.float32 or tuple(probs.shape) != (B, H, L, L) \
+            or not probs.is_contiguous():
+        raise ValueError("probs must be a contiguous float32 [B, H, L, L] GPU tensor")
+    args = _marshal(q, k, q, mask, rand_attn, block, r, q, stream, pad=pad_to_block)
+    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0)
+    # (q, k, mask, rand_attn, B, H, L, d, block, r, probs, stream, dtype, flags)
+    cargs = [args[0], args[1], args[3], args[4]] + list(args[5:11]) + [probs.data_ptr(), args[12], args[13], flags]
+    with torch.cuda.device(q.device):
+        st = lib().bbsa_attention_probs(*cargs)
+    _status(st, "bbsa_attention_probs", L, block, r, False)
+    return probs, st
 
 
 def bbsa_forward_noalloc(q, k, v, mask, rand_attn, block: int, r: int, out, stream=None,

@@ -222,6 +222,28 @@ int bbsa_forward_ex(const void *q, const void *k, const void *v, const float *ma
                     void *out, float *lse, hipStream_t stream, bbsa_dtype dtype, unsigned flags);
 
 /*
+ * The attention probabilities as a dense matrix (output_attentions).
+ *
+ * [BP] section "三类注意力组合全局 局部 随机": the block-sparse weights are
+ * scattered back into a full (batch, heads, L, L) attention matrix for
+ * callers that ask for the attention outputs; section "使用限制与注意事项":
+ * most of that matrix is zero and carries no gradient.  probs[b, h, t, u] is
+ * the softmax weight of key u in query row t (the scores, padding bias,
+ * options and pattern of bbsa_forward_ex with the same arguments and flags),
+ * exactly 0 for every key block outside the row's pattern.  Computed in fp32
+ * from q and k alone (each row's max and sum are formed in fp32 over the
+ * attended keys, relative to the row's largest padding bias, so rows whose
+ * keys all share one mask value keep fp32 precision); v is not needed.
+ *
+ * probs: device float32 [B, H, L, L], 4-byte aligned, caller-owned, fully
+ * overwritten (B * H * L * L * 4 bytes: an inspection path for moderate L).
+ * Other arguments, validation and status codes as bbsa_forward_ex.
+ */
+int bbsa_attention_probs(const void *q, const void *k, const float *mask, const int32_t *rand_attn,
+                         int B, int H, int L, int d, int block, int r, float *probs,
+                         hipStream_t stream, bbsa_dtype dtype, unsigned flags);
+
+/*
  * bbsa_forward for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  *
