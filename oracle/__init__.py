@@ -23,7 +23,7 @@ from .planner import (SplitMix64, plan_rand_attn, check_rand_attn, candidate_blo
                       truncate_plan)
 from .attention import (
     block_mask, token_mask, key_bias, uses_full_fallback, forward, full_attention,
-    attended_key_counts, pair_bias, forward_padded,
+    attended_key_counts, pair_bias, forward_padded, backward, backward_padded,
 )
 
 __all__ = [
@@ -31,4 +31,5 @@ __all__ = [
     "truncate_plan",
     "block_mask", "token_mask", "key_bias", "uses_full_fallback", "forward",
     "full_attention", "attended_key_counts", "pair_bias", "forward_padded",
+    "backward", "backward_padded",
 ]

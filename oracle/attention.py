@@ -223,6 +223,72 @@ def forward_padded(q, k, v, mask, rand_attn, block: int, **kw):
     return tuple(out)
 
 
+def backward(q, k, v, mask, rand_attn, block: int, dout, allow_fallback: bool = True,
+             query_key_mask: bool = False):
+    """Gradients of the forward with respect to q, k and v, in float64.
+
+    "models 仓库中的 BigBird…", section "梯度检查点的实现方式": training goes
+    through this operator's backward (the encoder can recompute the forward
+    instead of storing it); "BigBirdPegasus…", section "使用限制与注意事项":
+    the sparse probability matrix itself carries no gradient, so the
+    gradients are those of out = P V with P the masked row softmax.  Written
+    from the definition: with S the scores plus bias (excluded entries -inf),
+    P = softmax(S), O = P V and dO the gradient of the output,
+
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(dO * O)),
+        dQ = dS K,     dK = dS^T Q
+
+    (no internal scale; the padding bias and the block mask do not depend on
+    q or k).  Arguments as ``forward``; dout like q.  Returns (dq, dk, dv),
+    float64 ``[B, H, L, d]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    B, H, L, d = q.shape
+    if L % block != 0:
+        raise ValueError(f"sequence length {L} is not a multiple of block size {block}")
+    nb = L // block
+    r = 0 if rand_attn is None else int(np.asarray(rand_attn).shape[2])
+    full = allow_fallback and uses_full_fallback(L, block, r)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(H):
+        if full:
+            M = np.ones((nb, nb), dtype=bool)
+        else:
+            M = block_mask(nb, None if rand_attn is None else np.asarray(rand_attn)[h])
+        seen = np.kron(M.astype(np.int8), np.ones((block, block), np.int8)).astype(bool)
+        for b in range(B):
+            mb = None if mask is None else np.asarray(mask)[b]
+            S = q[b, h] @ k[b, h].T + pair_bias(mb, np.arange(L), L, query_key_mask)
+            S[~seen] = -np.inf
+            P = _softmax_rows(S)
+            O = P @ v[b, h]
+            dv[b, h] = P.T @ do[b, h]
+            dP = do[b, h] @ v[b, h].T
+            dS = P * (dP - (do[b, h] * O).sum(axis=-1, keepdims=True))
+            dq[b, h] = dS @ k[b, h]
+            dk[b, h] = dS.T @ q[b, h]
+    return dq, dk, dv
+
+
+def backward_padded(q, k, v, mask, rand_attn, block: int, dout, **kw):
+    """``backward`` for a length that need not be a multiple of the block:
+    the zero padding of ``forward_padded`` (mask 0 on the padding), a zero
+    output gradient on the padded rows (they are cut off the output), then
+    the gradients of the first L rows."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, d = q.shape
+    Lp = -(-L // block) * block
+    pad = ((0, 0), (0, 0), (0, Lp - L), (0, 0))
+    m = np.ones((B, L)) if mask is None else np.asarray(mask, dtype=np.float64).reshape(B, L)
+    mp = np.concatenate([m, np.zeros((B, Lp - L))], axis=1)
+    g = backward(np.pad(q, pad), np.pad(np.asarray(k, np.float64), pad), np.pad(np.asarray(v, np.float64), pad),
+                 mp, rand_attn, block, np.pad(np.asarray(dout, np.float64), pad), **kw)
+    return tuple(x[:, :, :L] for x in g)
+
+
 def full_attention(q, k, v, mask):
     """Plain dense attention ``softmax(Q K^T + bias) V`` with the key bias,
     float64 -- the "original_full" reference ("BigBirdPegasus…", section
