@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.bbsa_attention_probs.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 6 + \
             [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint]
         L.bbsa_attention_probs.restype = ctypes.c_int
+        L.bbsa_backward.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 5 + \
+            [ctypes.c_int, ctypes.c_uint]
+        L.bbsa_backward.restype = ctypes.c_int
         L.bbsa_status_string.argtypes = [ctypes.c_int]
         L.bbsa_status_string.restype = ctypes.c_char_p
         L.bbsa_release_workspace.argtypes = []
@@ -277,6 +280,36 @@ def bbsa_attention_probs(q, k, mask, rand_attn, block: int, r: int, probs=None, 
         st = lib().bbsa_attention_probs(*cargs)
     _status(st, "bbsa_attention_probs", L, block, r, False)
     return probs, st
+
+
+def bbsa_backward(q, k, v, out, dout, lse, mask, rand_attn, block: int, r: int, dq=None, dk=None, dv=None,
+                  delta=None, stream=None, pad_to_block: bool = False, query_key_mask: bool = False):
+    """Gradients (dq, dk, dv) of the forward's output; ``out`` and ``lse``
+    come from ``bbsa_forward_ex`` with the same arguments (see
+    include/bbsa.h).  Returns ``(dq, dk, dv, status)``."""
+    import torch
+    B, H, L, d = q.shape
+    for t in (out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("out and dout must be contiguous GPU tensors shaped and typed like q")
+    if not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, L] GPU tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous GPU tensors shaped and typed like q")
+    if delta is None:
+        delta = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    args = _marshal(q, k, v, mask, rand_attn, block, r, out, stream, pad=pad_to_block)
+    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0)
+    cargs = [args[0], args[1], args[2], out.data_ptr(), dout.data_ptr(), lse.data_ptr(), args[3], args[4]] + \
+        list(args[5:11]) + [dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), args[12], args[13], flags]
+    with torch.cuda.device(q.device):
+        st = lib().bbsa_backward(*cargs)
+    _status(st, "bbsa_backward", L, block, r, False)
+    return dq, dk, dv, st
 
 
 def bbsa_forward_noalloc(q, k, v, mask, rand_attn, block: int, r: int, out, stream=None,

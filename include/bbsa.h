@@ -244,6 +244,36 @@ int bbsa_attention_probs(const void *q, const void *k, const float *mask, const 
                          hipStream_t stream, bbsa_dtype dtype, unsigned flags);
 
 /*
+ * Backward pass: the gradients of bbsa_forward_ex's output with respect to
+ * q, k and v.
+ *
+ * [BB] section "梯度检查点的实现方式": the encoder is trained through this
+ * operator and may recompute its forward instead of storing activations;
+ * [BP] section "使用限制与注意事项": the sparse attention matrix carries no
+ * gradient of its own.  With P the pattern's row softmax (bias included),
+ * out = P V and dout the gradient of out:
+ *   dv = P^T dout,  ds = P * (dout v^T - rowsum(dout * out)),
+ *   dq = ds k,  dk = ds^T q.
+ * P is recomputed from q, k and the forward's row log-sum-exp, so the
+ * forward must have been run with the same arguments and flags and its
+ * `out` and `lse` passed here.
+ *
+ * q, k, v, out, dout: device bf16 [B, H, L, d], 16-byte aligned.
+ * lse:   device float32 [B, H, L] from bbsa_forward_ex.
+ * dq, dk, dv: device bf16 [B, H, L, d], caller-owned, fully overwritten.
+ * delta: device float32 [B, H, L], caller-owned scratch the call overwrites
+ *        (rowsum(dout * out)).
+ * mask, rand_attn, shapes, flags: as for bbsa_forward_ex.
+ *
+ * bf16 only (BBSA_ERR_UNSUPPORTED for BBSA_F32).  Other errors as
+ * bbsa_forward_ex.  Enqueues three kernels on `stream`; allocates nothing.
+ */
+int bbsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                  const float *lse, const float *mask, const int32_t *rand_attn, int B, int H, int L,
+                  int d, int block, int r, void *dq, void *dk, void *dv, float *delta,
+                  hipStream_t stream, bbsa_dtype dtype, unsigned flags);
+
+/*
  * bbsa_forward for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  *

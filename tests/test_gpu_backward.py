@@ -1,0 +1,125 @@
+"""Parity of the bf16 backward (bbsa_backward) with the oracle's float64
+gradients on MI355X ("models 仓库中的 BigBird…", section "梯度检查点的实现方式";
+"BigBirdPegasus…", section "使用限制与注意事项").
+
+The GPU path runs bbsa_forward_ex (bf16 output and fp32 row log-sum-exp),
+then bbsa_backward; the oracle differentiates the float64 definition at the
+same bf16 inputs and output gradient.
+
+Tolerance (derived from the arithmetic, for each of dq, dk, dv with s the
+largest magnitude of the oracle's gradient, at least 1): max abs <= 2e-2 s
+and mean abs <= 2e-3 s.  The GPU path's errors are relative to the
+gradient's scale: P carries the forward lse's error (the bf16 path sums
+bf16-rounded probabilities: up to 2^-9 relative), rowsum(dout * out) uses
+the forward's bf16 output (2^-9 relative per element), and ds and p are
+rounded to bf16 (2^-9) before the products that accumulate them in fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_bbsa_amd import bbsa, workloads
+from gpu_helpers import PARITY_LOG, announce, plans, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2e-2
+MEAN_REL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bbsa.lib()
+
+
+def bf16_exact(x):
+    return workloads.round_to_bf16(x)
+
+
+def run_backward(inp, dout, block, r, plan, pad=False, qk=False):
+    q, k, v, do = (to_dev(x, torch.bfloat16) for x in (inp["q"], inp["k"], inp["v"], dout))
+    mask = to_dev(inp["mask"], torch.float32)
+    ra = torch.from_numpy(plan).cuda() if plan is not None else None
+    out, lse, st = bbsa.bbsa_forward_ex(q, k, v, mask, ra, block, r, return_lse=True, pad_to_block=pad,
+                                        query_key_mask=qk, warn_fallback=False)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(q, float("nan"))
+    dv = torch.full_like(q, float("nan"))
+    dq, dk, dv, st2 = bbsa.bbsa_backward(q, k, v, out, do, lse, mask, ra, block, r, dq=dq, dk=dk, dv=dv,
+                                         pad_to_block=pad, query_key_mask=qk)
+    torch.cuda.synchronize()
+    assert st == st2
+    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)], st
+
+
+def check(got, want, what):
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        assert np.isfinite(g).all(), f"{what} {name}: non-finite (unwritten?) entries"
+        s = max(1.0, float(np.abs(w).max()))
+        err = np.abs(g - w)
+        announce(f"{what} {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} scale={s:.3g}")
+        PARITY_LOG.append((f"{what} {name}", int(np.prod(g.shape[:-1])), float(err.max()), float(err.mean())))
+        assert err.max() <= MAX_REL * s, f"{what} {name}: max abs {err.max()} (scale {s})"
+        assert err.mean() <= MEAN_REL * s, f"{what} {name}: mean abs {err.mean()} (scale {s})"
+
+
+CASES = [
+    # B, H, L, block, r, valid, pad, qk, seed
+    (2, 2, 1024, 64, 3, (1024, 700), False, False, 1),
+    (1, 3, 2048, 128, 2, (1900,), False, False, 2),
+    (2, 2, 1536, 64, 3, (1536, 900), False, True, 3),     # query x key
+    (2, 2, 1000, 64, 3, (1000, 937), True, False, 4),     # ragged length
+    (1, 2, 1100, 64, 3, (1050,), True, True, 5),          # ragged + query x key
+    (1, 2, 704, 64, 3, (650,), False, False, 6),          # short: full attention
+    (1, 2, 4096, 64, 3, (3500,), False, False, 7),        # long global rows and columns
+    (1, 2, 2048, 64, 12, (2048,), False, False, 8),       # many random blocks per row
+]
+
+
+@pytest.mark.parametrize("B,H,L,block,r,valid,pad,qk,seed", CASES)
+def test_backward_matches_oracle(B, H, L, block, r, valid, pad, qk, seed):
+    announce(f"backward B{B} H{H} L{L} block{block} r{r} valid={valid} pad={pad} qk={qk}")
+    inp = workloads.make_case(B, H, L, 64, 200 + seed, valid=valid)
+    rng = np.random.Generator(np.random.PCG64(300 + seed))
+    dout = bf16_exact(rng.standard_normal((B, H, L, 64)).astype(np.float32))
+    nb = -(-L // block)
+    full = L <= (5 + 2 * r) * block
+    cplan, oplan = plans(H, nb, r, seed)
+    got, st = run_backward(inp, dout, block, r, None if full else cplan, pad=pad, qk=qk)
+    assert st == (bbsa.BBSA_OK_FULL_FALLBACK if full else bbsa.BBSA_OK)
+    f = oracle.backward_padded if pad else oracle.backward
+    want = f(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block, dout, query_key_mask=qk)
+    check(got, want, f"backward L{L} pad={pad} qk={qk}")
+
+
+def test_backward_bigbird_base_workload():
+    # The BigBird-base workload (B4 H12 L4096, padded sequences) through the
+    # backward; every gradient row of four (batch, head) pairs on different
+    # XCD lanes is compared.
+    w = workloads.WORKLOADS[2]
+    announce("backward BigBird-base workload")
+    inp = workloads.make_inputs(2)
+    rng = np.random.Generator(np.random.PCG64(400))
+    dout = bf16_exact(rng.standard_normal(inp["q"].shape).astype(np.float32))
+    cplan, oplan = plans(w.H, w.nb, w.r, w.plan_seed)
+    got, st = run_backward(inp, dout, w.block, w.r, cplan)
+    assert st == bbsa.BBSA_OK
+    for g in got:
+        assert np.isfinite(g).all()
+    for bh in (0, 13, 30, 47):
+        b, h = divmod(bh, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        want = oracle.backward(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["mask"][b:b + 1], oplan[h:h + 1],
+                               w.block, dout[sl])
+        check([g[sl] for g in got], want, f"backward {w.name} pair {bh}")
+
+
+def test_backward_refuses_fp32():
+    q = torch.zeros((1, 1, 1024, 64), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((1, 1, 1024), dtype=torch.float32, device="cuda")
+    ra = torch.from_numpy(bbsa.bbsa_plan_rand_attn(1, 16, 3, 0)).cuda()
+    with pytest.raises(ValueError):
+        bbsa.bbsa_backward(q, q, q, q, q, lse, None, ra, 64, 3)
