@@ -248,6 +248,48 @@ class Runner:
         self.torch.cuda.empty_cache()
 
 
+def backward_leg(run, args, torch, bbsa):
+    """Time one backward step (the row kernel, the dq kernel and the dk/dv
+    kernel) on the headline workload's inputs, after a forward that saved
+    the output and the row log-sum-exp.  Useful flops: 2.5 times the
+    forward's (the five products of the gradients; the recompute of the
+    scores and the probability gradients in both kernels is not counted)."""
+    w = run.w
+    q, k, v, _ = run.sets[0]
+    dout = torch.randn_like(q)
+    out, lse, _ = bbsa.bbsa_forward_ex(q, k, v, run.mask, run.ra, w.block, w.r, return_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+
+    def step():
+        bbsa.bbsa_backward(q, k, v, out, dout, lse, run.mask, run.ra, w.block, w.r, dq=dq, dk=dk, dv=dv,
+                           delta=delta, stream=run.stream)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.preroll:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    n = max(1, args.steps // 4)
+    for _ in range(max(1, args.warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(run.stream)
+    for _ in range(n):
+        step()
+    e1.record(run.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 2.5 * useful_flops(w.B, w.H, w.nb, w.block, w.d, w.r)
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"{w.name} backward: step {ms * 1e3:.2f} us; {tf:.1f} useful TFLOP/s; MFMA frac {tf / PEAK_BF16_TFLOPS:.4f}")
+    return {"step_us": round(ms * 1e3, 3), "steps": n, "useful_gflop_per_step": round(flops / 1e9, 3),
+            "useful_tflops": round(tf, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +298,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="headline workload id 1..5 (default 2)")
     ap.add_argument("--others", default="3,4,5",
                     help="other workload ids timed in the same run ('' for none)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--preroll", type=float, default=0.3,
                     help="seconds of untimed steps before each workload's warm-up (clock ramp)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
@@ -305,6 +348,9 @@ def main():
     log(f"{w.name}: step {ms * 1e3:.2f} us (p10/p50/p90 {p10}/{p50}/{p90}, warm {warm_us:.1f}); "
         f"{value:.1f} useful TFLOP/s; frac {roof['frac']} ({roof['bound']}); "
         f"MFMA {roof['mfma_frac']} HBM {roof['hbm_frac']}")
+    backward = None
+    if not args.no_backward and w.dtype == "bf16":
+        backward = backward_leg(run, args, torch, bbsa)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
@@ -351,7 +397,8 @@ def main():
                    "warm_step_us": round(warm_us, 2),
                    "preroll": {"seconds": args.preroll, "steps": pre},
                    "parallelism": "none (1 GPU)",
-                   "other_workloads": others},
+                   "other_workloads": others,
+                   "backward": backward},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

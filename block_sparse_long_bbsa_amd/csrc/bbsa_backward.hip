@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "bbsa.h"
 #include "bbsa_schedule.h"
@@ -59,6 +60,9 @@ __device__ inline int swz_t(int row) { return ((row >> 1) & 1) << 2; }
 
 __device__ inline int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() & 63; }
 
+constexpr int kChunkBlocks = 8;                 // blocks per chunk of a global row or column
+constexpr int kMaskBytes = 256;                 // per-step array of 64 floats (lanes 32..63 repeat 0..31)
+
 struct BwdParams {
   const bf16_t *q, *k, *v, *o, *dout;
   const float *lse;          // [B, H, L]
@@ -66,11 +70,65 @@ struct BwdParams {
   const int32_t *rand_attn;  // [H, nb-2, r] or null (fallback)
   float *delta;              // [B, H, L]
   bf16_t *dq, *dk, *dv;
+  float *ws;                 // split partials of the global rows (dq) and columns (dk, dv)
   int B, H, L, nb, block, r;
   int full;                  // every block attends every block
   int qk;                    // query x key masking
   int tiles;                 // 32-row tiles per block
+  int chunks;                // chunks of a global row or column (1: no partials)
+  int n_grows;               // global rows (and columns) per pair: 2, or nb on the fallback
+  int lanes;                 // XCD lanes: 8 when there are at least 8 pairs, else 1
+  int glob_items;            // per pair: n_grows * tiles * chunks
+  int mid_items;             // per pair: (nb - 2) * tiles (0 on the fallback)
+  int n_glob_lane;           // global items before the first middle item, per XCD lane
+  int64_t n_part;            // partials per gradient
 };
+
+// Work item: a 32-row tile of block blk (a query block for dq, a key block
+// for dk/dv) of pair bh; a global row or column is split into `chunks`
+// ranges of blocks.  Workgroup w runs on XCD w % 8 and, with the XCD lanes,
+// serves only the pairs x, x + 8, ... (x = w % 8), so the tiles a pair
+// re-reads stay in one L2; the global items of a lane come first.
+struct BwdItem {
+  int bh, blk, tile, chunk, g;
+  bool glob;
+};
+__device__ inline BwdItem decode(const BwdParams &p, int wg) {
+  const int x = wg % p.lanes, slot = wg / p.lanes;
+  BwdItem it;
+  it.chunk = 0;
+  it.g = 0;
+  if (slot < p.n_glob_lane) {
+    const int j = slot / p.glob_items, loc = slot % p.glob_items;
+    it.bh = x + j * p.lanes;
+    it.glob = true;
+    it.g = loc / (p.tiles * p.chunks);
+    const int rem = loc % (p.tiles * p.chunks);
+    it.tile = rem / p.chunks;
+    it.chunk = rem % p.chunks;
+    it.blk = p.full ? it.g : (it.g == 0 ? 0 : p.nb - 1);
+  } else if (p.mid_items > 0) {
+    const int s2 = slot - p.n_glob_lane;
+    const int j = s2 / p.mid_items, loc = s2 % p.mid_items;
+    it.bh = x + j * p.lanes;
+    it.glob = false;
+    it.blk = 1 + loc / p.tiles;
+    it.tile = loc % p.tiles;
+  } else {
+    it.bh = 0x7fffffff;   // idle
+    it.glob = false;
+    it.blk = it.tile = 0;
+  }
+  // Uniform by construction; stated so that addresses built from them stay
+  // in scalar registers.
+  it.bh = __builtin_amdgcn_readfirstlane(it.bh);
+  it.blk = __builtin_amdgcn_readfirstlane(it.blk);
+  it.tile = __builtin_amdgcn_readfirstlane(it.tile);
+  it.chunk = __builtin_amdgcn_readfirstlane(it.chunk);
+  it.g = __builtin_amdgcn_readfirstlane(it.g);
+  it.glob = __builtin_amdgcn_readfirstlane((int)it.glob) != 0;
+  return it;
+}
 
 // Per-lane DMA state of one 32 x 64 tile: lane l of instruction u loads row
 // 8u + l/8 of the tile into LDS position tile + 1024u + 16l.
@@ -85,10 +143,15 @@ struct TileDma {
   }
 };
 
+// A row index past every supported length (L <= 2^24): its transfers are
+// out of the buffer's range, so they write zeros and read no memory.
+constexpr int kNoRow = 1 << 24;
+
 // Rows row0 .. row0+31 of a [L, 64] bf16 matrix (buffer resource rs) into
-// LDS; rows at or past L read as zeros.
+// LDS; rows at or past L read as zeros (the offset is range-checked).  The
+// offsets are 32-bit unsigned: row0 * 128 reaches 2^31 for kNoRow.
 __device__ inline void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, const TileDma &t, int row0, bool tsw) {
-  const int base = row0 * (kD * 2);
+  const int base = (int)((unsigned)row0 * (kD * 2));
   if (tsw) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_t + base, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_t + base, 0, 1024, 0);
@@ -101,11 +164,18 @@ __device__ inline void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, c
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_r[3] + base, 0, 3072, 0);
   }
 }
+// Floats pos0 + (lane % 32) of a float buffer resource into LDS (64 floats,
+// the upper 32 repeating the lower); positions past the range read as 0.
+__device__ inline void dma_floats(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int pos0, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 4, (int)(4u * (unsigned)(pos0 + (lane & 31))), 0, 0, 0);
+}
 
-// A operands of the rows of an R-swizzled tile: row c, d = 16kk + 8h .. +7.
+// A operands of the rows of a tile: row c, d = 16kk + 8h .. +7.
+template <bool TSW>
 __device__ inline void read_rows(const unsigned char *src, int c, int h, bf16x8 (&a)[4]) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) a[kk] = *(const bf16x8 *)(src + c * 128 + 16 * ((2 * kk + h) ^ swz_r(c)));
+  for (int kk = 0; kk < 4; ++kk)
+    a[kk] = *(const bf16x8 *)(src + c * 128 + 16 * ((2 * kk + h) ^ (TSW ? swz_t(c) : swz_r(c))));
 }
 
 // A operands of the transposed T-swizzled tile X (rows r, columns d): for
@@ -171,7 +241,8 @@ __device__ inline void load_b_rows(const bf16_t *base, int L, int row0, int c, i
 }
 
 // Store a 32x32 MFMA result holding X^T (rows d = 32dt + 8j + 4h + i, column
-// = row c of X) as bf16 rows row0 + c of a [L, 64] matrix.
+// = row c of X): as bf16 rows row0 + c of a [L, 64] matrix, or as the fp32
+// [32][64] partial `part`.
 __device__ inline void store_t(bf16_t *base, int L, int row0, int c, int h, const f32x16 (&x)[2]) {
   const int row = row0 + c;
   if (row >= L) return;
@@ -183,32 +254,55 @@ __device__ inline void store_t(bf16_t *base, int L, int row0, int c, int h, cons
       *(bf16x4 *)(base + (int64_t)row * kD + 32 * dt + 8 * j + 4 * h) = __builtin_convertvector(y, bf16x4);
     }
 }
+__device__ inline void store_partial(float *part, int c, int h, const f32x16 (&x)[2]) {
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 y = {x[dt][4 * j], x[dt][4 * j + 1], x[dt][4 * j + 2], x[dt][4 * j + 3]};
+      *(f32x4 *)(part + c * kD + 32 * dt + 8 * j + 4 * h) = y;
+    }
+}
 
 __device__ inline float mask_at(const BwdParams &p, const float *mrow, int pos) {
   return pos < p.L ? (mrow ? mrow[pos] : 1.0f) : 0.0f;
 }
 
-// D[t] = sum_e dO[t, e] out[t, e] (one thread per row).
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, kBufferWord3);
+}
+
+// Wait until at most KEEP vector-memory operations are outstanding: the
+// transfers of the next step (issued for every step, past the end too, as
+// out-of-range transfers of kNoRow), so that this step's have landed.
+// Memory loads complete in issue order.
+template <int KEEP>
+__device__ inline void wait_step() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
+}
+__device__ inline void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// D[t] = sum_e dO[t, e] out[t, e]: eight threads per row, 16 bytes each.
 __global__ __launch_bounds__(256) void bbsa_bwd_delta(BwdParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= (int64_t)p.B * p.H * p.L) return;
-  const bf16x8 *a = (const bf16x8 *)(p.dout + row * kD);
-  const bf16x8 *b = (const bf16x8 *)(p.o + row * kD);
+  const int64_t rows = (int64_t)p.B * p.H * p.L;
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
   float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kD / 8; ++i) {
-    const bf16x8 x = a[i], y = b[i];
+  if (row < rows) {
+    const bf16x8 x = *(const bf16x8 *)(p.dout + row * kD + 8 * part);
+    const bf16x8 y = *(const bf16x8 *)(p.o + row * kD + 8 * part);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
   }
-  p.delta[row] = acc;
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && part == 0) p.delta[row] = acc;
 }
 
 // Key block of list position t of middle query block i (the forward's list:
-// the two global blocks, the window without them, the plan's blocks), or the
-// block itself for a full row.
-__device__ inline int list_block(const BwdParams &p, const int32_t *plan_row, int i, int t, bool full_row) {
-  if (full_row) return t;
+// the two global blocks, the window without them, the plan's blocks).
+__device__ inline int list_block(const BwdParams &p, const int32_t *plan_row, int i, int t) {
   if (t == 0) return 0;
   if (t == 1) return p.nb - 1;
   const int nw = (i == 1 || i == p.nb - 2) ? 2 : 3;
@@ -217,150 +311,199 @@ __device__ inline int list_block(const BwdParams &p, const int32_t *plan_row, in
   return min(max(plan_row[t - 2 - nw], 0), p.nb - 1);
 }
 
-// dQ: one wavefront per 32-query tile; workgroups of one wavefront.  The
-// tiles of the full rows (blocks 0 and nb-1, or every block on the fallback)
-// come first in the grid.
-__global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 3 * kTile];   // per slot: K rows, K transposed, V rows
-  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
-  const int n_full_rows = p.full ? p.nb : 2;
-  const int per_bh_full = n_full_rows * p.tiles;
-  const int per_bh = p.nb * p.tiles;
-  int w = (int)blockIdx.x;
-  int bh, i, tile;
-  if (w < p.B * p.H * per_bh_full) {
-    bh = w / per_bh_full;
-    const int x = w % per_bh_full;
-    const int g = x / p.tiles;
-    tile = x % p.tiles;
-    i = p.full ? g : (g == 0 ? 0 : p.nb - 1);
-  } else {
-    w -= p.B * p.H * per_bh_full;
-    const int per_bh_mid = per_bh - per_bh_full;
-    bh = w / per_bh_mid;
-    const int x = w % per_bh_mid;
-    i = 1 + x / p.tiles;
-    tile = x % p.tiles;
+template <int S>
+using SlotId = std::integral_constant<int, S>;
+
+// Runs step(SlotId<st % 3>, st) for st = 0 .. n-1 with the slot as a
+// compile-time constant, so that every LDS access names one of three
+// separate arrays and the compiler's own waits for the transfers into LDS
+// wait for the right slot only.
+template <class Step>
+__device__ inline void run_steps(int n, Step &&step) {
+  int st = 0;
+  for (; st + 3 <= n; st += 3) {
+    step(SlotId<0>{}, st);
+    step(SlotId<1>{}, st + 1);
+    step(SlotId<2>{}, st + 2);
   }
+  if (st < n) step(SlotId<0>{}, st);
+  if (st + 1 < n) step(SlotId<1>{}, st + 1);
+}
+
+// dQ: one wavefront per 32-query tile; workgroups of one wavefront.  Three
+// LDS slots, each K (T swizzle) and V (R swizzle) of one step and the key
+// mask: the transfers of step st + 2 go out while step st computes.
+template <bool MASKED>
+__global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
+  const BwdItem it = decode(p, (int)blockIdx.x);
+  if (it.bh >= p.B * p.H) return;
+  __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * kTile], kv1[2 * kTile], kv2[2 * kTile];
+  __shared__ __attribute__((aligned(256))) unsigned char mk0[kMaskBytes], mk1[kMaskBytes], mk2[kMaskBytes];
+  auto kv = [&](auto S) -> unsigned char * {
+    if constexpr (decltype(S)::value == 0) return kv0;
+    else if constexpr (decltype(S)::value == 1) return kv1;
+    else return kv2;
+  };
+  auto mk = [&](auto S) -> unsigned char * {
+    if constexpr (decltype(S)::value == 0) return mk0;
+    else if constexpr (decltype(S)::value == 1) return mk1;
+    else return mk2;
+  };
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int bh = it.bh, i = it.blk;
   const int b = bh / p.H, hh = bh % p.H;
-  const bool full_row = p.full || i == 0 || i == p.nb - 1;
-  const int q0 = i * p.block + tile * kT;
+  const int q0 = i * p.block + it.tile * kT;
   const int64_t seq = (int64_t)p.L * kD;
-  const float *mrow = p.mask ? p.mask + (int64_t)b * p.L : nullptr;
-  const int32_t *plan_row = full_row ? nullptr : p.rand_attn + ((int64_t)hh * (p.nb - 2) + (i - 1)) * p.r;
-  const int n_blocks = full_row ? p.nb : (2 + ((i == 1 || i == p.nb - 2) ? 2 : 3) + p.r);
-  const int steps_per_block = p.block / kT;
-  const int n_steps = n_blocks * steps_per_block;
+  const float *mrow = MASKED ? p.mask + (int64_t)b * p.L : nullptr;
+  const int32_t *plan_row = it.glob ? nullptr : p.rand_attn + ((int64_t)hh * (p.nb - 2) + (i - 1)) * p.r;
+  const int spb = p.block / kT, lg_spb = spb >> 1;   // 2 or 4 steps per block
+  // List positions walked: a chunk of the blocks for a global row, the
+  // forward's list for a middle row.
+  int pos0 = 0, pos1;
+  if (it.glob) {
+    pos0 = it.chunk * p.nb / p.chunks;
+    pos1 = (it.chunk + 1) * p.nb / p.chunks;
+  } else {
+    pos1 = 2 + ((i == 1 || i == p.nb - 2) ? 2 : 3) + p.r;
+  }
+  const int n_steps = __builtin_amdgcn_readfirstlane((pos1 - pos0) * spb);
+  // The middle row's key blocks, lane t holding list position t (at most 64).
+  const int blocks = it.glob ? 0 : list_block(p, plan_row, i, min(lane, pos1 - 1));
+  auto key_of = [&](int st) {
+    const int pos = pos0 + (st >> lg_spb);
+    const int row =
+        (it.glob ? pos : __builtin_amdgcn_readlane(blocks, min(pos, 63))) * p.block + (st & (spb - 1)) * kT;
+    return __builtin_amdgcn_readfirstlane(st < n_steps ? row : kNoRow);
+  };
 
   TileDma dma;
   dma.init(lane);
   int toff[2];
   tr_offsets(lane, toff);
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.k + bh * seq), (short)0, p.L * kD * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.v + bh * seq), (short)0, p.L * kD * 2, kBufferWord3);
+  const auto krs = rsrc(p.k + bh * seq, seq * 2);
+  const auto vrs = rsrc(p.v + bh * seq, seq * 2);
+  const auto mrs = rsrc(mrow, (int64_t)p.L * 4);
 
   // Q and dO of the tile (B operands), and the query column's lse (log2
-  // units, with the query x key constant taken out), D and mask factor.
+  // units, the query x key constant taken out), D and mask factor.
   bf16x8 qf[4], df[4];
   load_b_rows(p.q + bh * seq, p.L, q0, c, h, qf);
   load_b_rows(p.dout + bh * seq, p.L, q0, c, h, df);
   const int qrow = q0 + c;
   const bool qlive = qrow < p.L;
   const float mq = p.qk ? (qlive ? mask_at(p, mrow, qrow) : 0.0f) : 1.0f;
-  const float lse2 = qlive ? (p.lse[(int64_t)bh * p.L + qrow] - (p.qk ? kPadBias * (1.0f - mq) : 0.0f)) * kLog2e : 0.0f;
+  const float lse2 =
+      qlive ? (p.lse[(int64_t)bh * p.L + qrow] - (p.qk ? kPadBias * (1.0f - mq) : 0.0f)) * kLog2e : 0.0f;
   const float dlt = qlive ? p.delta[(int64_t)bh * p.L + qrow] : 0.0f;
 
-  auto key_of = [&](int st) {
-    return list_block(p, plan_row, i, st / steps_per_block, full_row) * p.block + (st % steps_per_block) * kT;
-  };
-  auto issue = [&](int st) {
-    unsigned char *s = lds + (st & 1) * 3 * kTile;
+  auto issue = [&](auto S, int st) {
     const int key0 = key_of(st);
-    dma_rows(krs, s, dma, key0, false);
-    dma_rows(krs, s + kTile, dma, key0, true);
-    dma_rows(vrs, s + 2 * kTile, dma, key0, false);
+    dma_rows(krs, kv(S), dma, key0, true);
+    dma_rows(vrs, kv(S) + kTile, dma, key0, false);
+    if (MASKED) dma_floats(mrs, mk(S), key0, lane);
   };
+  constexpr int kPerStep = MASKED ? 9 : 8;
 
+  // Transfers go out for every step below n_steps + 2, so the compiler's
+  // own wait before each slot's reads also counts only that slot's.
   f32x16 dq[2] = {zero16(), zero16()};
-  issue(0);
-  for (int st = 0; st < n_steps; ++st) {
-    // The transfer of step st has landed; the LDS reads of step st-1 (the
-    // slot the next transfer overwrites) were consumed by its products.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (st + 1 < n_steps) issue(st + 1);
-    const unsigned char *s = lds + (st & 1) * 3 * kTile;
+  issue(SlotId<0>{}, 0);
+  issue(SlotId<1>{}, 1);
+  run_steps(n_steps, [&](auto S, int st) {
+    constexpr int NEXT2 = (decltype(S)::value + 2) % 3;
+    wait_step<kPerStep>();
+    const unsigned char *s = kv(S);
     const int key0 = key_of(st);
     bf16x8 kr[4], vr[4], kt[2][2];
-    read_rows(s, c, h, kr);
-    read_rows(s + 2 * kTile, c, h, vr);
-    read_tr(s + kTile, toff, kt);
+    read_rows<true>(s, c, h, kr);
+    read_rows<false>(s + kTile, c, h, vr);
+    read_tr(s, toff, kt);
+    f32x4 mkv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (MASKED) {
+        mkv[jj] = *(const f32x4 *)(mk(S) + 4 * (8 * jj + 4 * h));
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) mkv[jj][ii] = key0 + 8 * jj + 4 * h + ii < p.L ? 1.0f : 0.0f;
+      }
+    }
+    // The transfers of step st + 2 go into the slot step st - 1 read.
+    issue(SlotId<NEXT2>{}, st + 2);
     f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       sc = mfma(kr[kk], qf[kk], sc);   // S^T[key][query c]
       dp = mfma(vr[kk], df[kk], dp);   // dP^T[key][query c]
     }
-    // P^T and dS^T; register 4j + i is key key0 + 8j + 4h + i.
+    // P^T and dS^T; register 4jj + ii is key key0 + 8jj + 4h + ii.
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = key0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      const float bias = mq * (kPadBias * (1.0f - mask_at(p, mrow, key)));
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e] + bias, kLog2e, -lse2));
-      sc[e] = pr * (dp[e] - dlt);
-    }
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int e = 4 * jj + ii;
+        const float pr =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e] + mq * (kPadBias * (1.0f - mkv[jj][ii])), kLog2e, -lse2));
+        sc[e] = pr * (dp[e] - dlt);
+      }
     bf16x8 dsb[2];
     pack_b(sc, dsb);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) dq[dt] = mfma(kt[dt][ss], dsb[ss], dq[dt]);   // dQ^T[d][query c]
+  });
+  wait_all();   // the two transfers past the end
+  if (it.glob && p.chunks > 1) {
+    const int64_t idx = (((int64_t)bh * p.n_grows + it.g) * p.tiles + it.tile) * p.chunks + it.chunk;
+    store_partial(p.ws + idx * (kT * kD), c, h, dq);
+  } else {
+    store_t(p.dq + bh * seq, p.L, q0, c, h, dq);
   }
-  store_t(p.dq + bh * seq, p.L, q0, c, h, dq);
 }
 
 // dK, dV: one wavefront per 32-key tile.  The query blocks that attend key
-// block j: every block for a global key block (or on the fallback); else the
-// two global blocks, the window {j-1, j, j+1} (without repeating a global
-// one) and the middle blocks whose plan row picked j.
+// block j: a chunk of every block for a global key block (or on the
+// fallback); else the two global blocks, the window {j-1, j, j+1} (without
+// repeating a global one) and the middle blocks whose plan row picked j,
+// gathered in an LDS list and walked at least 64 blocks at a time.  Three
+// LDS slots, each Q and dO (T swizzle) of one step with the step's lse, D
+// and query mask values.
+template <bool QK>
 __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 4 * kTile];   // per slot: Q rows, Q tr, dO rows, dO tr
+  const BwdItem it = decode(p, (int)blockIdx.x);
+  if (it.bh >= p.B * p.H) return;
+  constexpr int kVec = 3 * kMaskBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char qd0[2 * kTile], qd1[2 * kTile], qd2[2 * kTile];
+  __shared__ __attribute__((aligned(256))) unsigned char vc0[kVec], vc1[kVec], vc2[kVec];
+  __shared__ int blist[128];
+  auto qd = [&](auto S) -> unsigned char * {
+    if constexpr (decltype(S)::value == 0) return qd0;
+    else if constexpr (decltype(S)::value == 1) return qd1;
+    else return qd2;
+  };
+  auto vc = [&](auto S) -> unsigned char * {
+    if constexpr (decltype(S)::value == 0) return vc0;
+    else if constexpr (decltype(S)::value == 1) return vc1;
+    else return vc2;
+  };
   const int lane = lane_id(), c = lane & 31, h = lane >> 5;
-  const int n_full_cols = p.full ? p.nb : 2;
-  const int per_bh_full = n_full_cols * p.tiles;
-  const int per_bh = p.nb * p.tiles;
-  int w = (int)blockIdx.x;
-  int bh, j, tile;
-  if (w < p.B * p.H * per_bh_full) {
-    bh = w / per_bh_full;
-    const int x = w % per_bh_full;
-    const int g = x / p.tiles;
-    tile = x % p.tiles;
-    j = p.full ? g : (g == 0 ? 0 : p.nb - 1);
-  } else {
-    w -= p.B * p.H * per_bh_full;
-    const int per_bh_mid = per_bh - per_bh_full;
-    bh = w / per_bh_mid;
-    const int x = w % per_bh_mid;
-    j = 1 + x / p.tiles;
-    tile = x % p.tiles;
-  }
+  const int bh = it.bh, j = it.blk;
   const int b = bh / p.H, hh = bh % p.H;
-  const bool full_col = p.full || j == 0 || j == p.nb - 1;
-  const int k0 = j * p.block + tile * kT;
+  const int k0 = j * p.block + it.tile * kT;
   const int64_t seq = (int64_t)p.L * kD;
   const float *mrow = p.mask ? p.mask + (int64_t)b * p.L : nullptr;
-  const int steps_per_block = p.block / kT;
+  const int spb = p.block / kT, lg_spb = spb >> 1;   // 2 or 4 steps per block
 
   TileDma dma;
   dma.init(lane);
   int toff[2];
   tr_offsets(lane, toff);
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.q + bh * seq), (short)0, p.L * kD * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t drs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.dout + bh * seq), (short)0, p.L * kD * 2, kBufferWord3);
+  const auto qrs = rsrc(p.q + bh * seq, seq * 2);
+  const auto drs = rsrc(p.dout + bh * seq, seq * 2);
+  const auto lrs = rsrc(p.lse + (int64_t)bh * p.L, (int64_t)p.L * 4);
+  const auto ers = rsrc(p.delta + (int64_t)bh * p.L, (int64_t)p.L * 4);
+  const auto mrs = rsrc(mrow, (int64_t)p.L * 4);
 
   // K and V of the tile (B operands: lane (c, h) = key k0 + c); the key
   // column's padding bias.
@@ -369,65 +512,68 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
   load_b_rows(p.v + bh * seq, p.L, k0, c, h, vf);
   const float kbias = kPadBias * (1.0f - mask_at(p, mrow, k0 + c));
 
-  // The query blocks, in three groups: the fixed ones (globals and the
-  // window, or all blocks), then plan rows found 64 entries at a time.
-  int fixed[5];
-  int n_fixed = 0;
-  if (!full_col) {
-    fixed[n_fixed++] = 0;
-    fixed[n_fixed++] = p.nb - 1;
-    for (int x = j - 1; x <= j + 1; ++x)
-      if (x > 0 && x < p.nb - 1) fixed[n_fixed++] = x;
-  }
-
   f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
-  // One query block: its query steps through LDS, accumulating dK and dV.
-  auto run_block = [&](int i) {
-    const int nst = steps_per_block;
-    auto issue = [&](int st) {
-      unsigned char *s = lds + (st & 1) * 4 * kTile;
-      const int row0 = i * p.block + st * kT;
-      dma_rows(qrs, s, dma, row0, false);
-      dma_rows(qrs, s + kTile, dma, row0, true);
-      dma_rows(drs, s + 2 * kTile, dma, row0, false);
-      dma_rows(drs, s + 3 * kTile, dma, row0, true);
+  constexpr int kPerStep = QK ? 11 : 10;
+  // Walk the query blocks of list positions [0, n) (block of position t:
+  // from the LDS list, or first + t for a range), 32 queries a step.
+  auto walk = [&](int n, bool from_list, int first) {
+    const int n_steps = __builtin_amdgcn_readfirstlane(n * spb);
+    auto row_of = [&](int st) {
+      const int t = min(st >> lg_spb, 127);
+      const int row = (from_list ? blist[t] : first + t) * p.block + (st & (spb - 1)) * kT;
+      return __builtin_amdgcn_readfirstlane(st < n_steps ? row : kNoRow);
     };
-    issue(0);
-    for (int st = 0; st < nst; ++st) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (st + 1 < nst) issue(st + 1);
-      const unsigned char *s = lds + (st & 1) * 4 * kTile;
-      const int row0 = i * p.block + st * kT;
+    auto issue = [&](auto S, int st) {
+      const int row0 = row_of(st);
+      dma_rows(qrs, qd(S), dma, row0, true);
+      dma_rows(drs, qd(S) + kTile, dma, row0, true);
+      dma_floats(lrs, vc(S), row0, lane);
+      dma_floats(ers, vc(S) + kMaskBytes, row0, lane);
+      if (QK) dma_floats(mrs, vc(S) + 2 * kMaskBytes, row0, lane);
+    };
+    issue(SlotId<0>{}, 0);
+    issue(SlotId<1>{}, 1);
+    run_steps(n_steps, [&](auto S, int st) {
+      constexpr int NEXT2 = (decltype(S)::value + 2) % 3;
+      wait_step<kPerStep>();
+      const unsigned char *s = qd(S);
+      const unsigned char *v = vc(S);
       bf16x8 qr[4], dr[4], qt[2][2], dt2[2][2];
-      read_rows(s, c, h, qr);
-      read_rows(s + 2 * kTile, c, h, dr);
-      read_tr(s + kTile, toff, qt);
-      read_tr(s + 3 * kTile, toff, dt2);
+      read_rows<true>(s, c, h, qr);
+      read_rows<true>(s + kTile, c, h, dr);
+      read_tr(s, toff, qt);
+      read_tr(s + kTile, toff, dt2);
+      // Register 4jj + ii is query row0 + 8jj + 4h + ii; its lse, D and mask
+      // value (rows past L read as 0: their Q and dO are zeros, so they add
+      // nothing).
+      f32x4 ls[4], dl[4], mqv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        ls[jj] = *(const f32x4 *)(v + 4 * (8 * jj + 4 * h));
+        dl[jj] = *(const f32x4 *)(v + kMaskBytes + 4 * (8 * jj + 4 * h));
+        if (QK) mqv[jj] = *(const f32x4 *)(v + 2 * kMaskBytes + 4 * (8 * jj + 4 * h));
+        else mqv[jj] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+      }
+      issue(SlotId<NEXT2>{}, st + 2);
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         sc = mfma(qr[kk], kf[kk], sc);   // S[query][key c]
         dp = mfma(dr[kk], vf[kk], dp);   // dP[query][key c]
       }
-      // Register 4jj + ii is query row0 + 8jj + 4h + ii.
-      f32x16 pm, dsv;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qrow = row0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        float pr = 0.0f, ds = 0.0f;
-        if (qrow < p.L) {
-          const float mq = p.qk ? mask_at(p, mrow, qrow) : 1.0f;
-          const float lse2 =
-              (p.lse[(int64_t)bh * p.L + qrow] - (p.qk ? kPadBias * (1.0f - mq) : 0.0f)) * kLog2e;
-          pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e] + mq * kbias, kLog2e, -lse2));
-          ds = pr * (dp[e] - p.delta[(int64_t)bh * p.L + qrow]);
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int e = 4 * jj + ii;
+          const float lse2 = (ls[jj][ii] - (QK ? kPadBias * (1.0f - mqv[jj][ii]) : 0.0f)) * kLog2e;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e] + mqv[jj][ii] * kbias, kLog2e, -lse2));
+          sc[e] = pr;
+          dp[e] = pr * (dp[e] - dl[jj][ii]);
         }
-        pm[e] = pr;
-        dsv[e] = ds;
-      }
       bf16x8 pb[2], db[2];
-      pack_b(pm, pb);
-      pack_b(dsv, db);
+      pack_b(sc, pb);
+      pack_b(dp, db);
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
@@ -435,35 +581,87 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
           dv[d2] = mfma(dt2[d2][ss], pb[ss], dv[d2]);   // dV^T[d][key c]
           dk[d2] = mfma(qt[d2][ss], db[ss], dk[d2]);    // dK^T[d][key c]
         }
-    }
+    });
+    wait_all();   // the two transfers past the end
   };
 
-  if (full_col) {
-    for (int i = 0; i < p.nb; ++i) run_block(i);
+  if (it.glob) {
+    const int first = it.chunk * p.nb / p.chunks;
+    walk((it.chunk + 1) * p.nb / p.chunks - first, false, first);
   } else {
-    for (int x = 0; x < n_fixed; ++x) run_block(fixed[x]);
-    // Plan rows that picked j (rows are middle blocks outside j's window,
-    // so none repeats a fixed block); a bad plan's entries are clamped as in
-    // the forward.
+    // The fixed blocks, then the plan rows that picked j, 64 entries of the
+    // plan per pass; the list is walked once it holds 64 blocks or the plan
+    // is done.  Rows of the plan are middle blocks outside j's window, so
+    // none repeats a fixed block (a clamped bad plan's repeats are skipped).
+    int n_fixed = 0;
+    int fixed[5];
+    fixed[n_fixed++] = 0;
+    fixed[n_fixed++] = p.nb - 1;
+    for (int x = j - 1; x <= j + 1; ++x)
+      if (x > 0 && x < p.nb - 1) fixed[n_fixed++] = x;
+    if (lane == 0)
+      for (int x = 0; x < n_fixed; ++x) blist[x] = fixed[x];
+    int n = n_fixed;
     const int32_t *plan_h = p.rand_attn + (int64_t)hh * (p.nb - 2) * p.r;
     const int n_entries = (p.nb - 2) * p.r;
-    for (int e0 = 0; e0 < n_entries; e0 += 64) {
-      const int e = e0 + lane;
-      const bool hit = e < n_entries && min(max(plan_h[min(e, n_entries - 1)], 0), p.nb - 1) == j;
-      unsigned long long bits = __builtin_amdgcn_ballot_w64(hit);
-      while (bits) {
-        const int l = __builtin_ctzll(bits);
-        bits &= bits - 1;
-        const int row = 1 + (e0 + l) / p.r;   // middle query block of that plan entry
-        // A clamped bad plan could pick a fixed block; it is counted once.
-        bool dup = false;
-        for (int x = 0; x < n_fixed; ++x) dup |= fixed[x] == row;
-        if (!dup) run_block(row);
+    for (int e0 = 0;; e0 += 64) {
+      if (e0 < n_entries) {
+        const int e = e0 + lane;
+        const bool hit = e < n_entries && min(max(plan_h[min(e, n_entries - 1)], 0), p.nb - 1) == j;
+        unsigned long long bits = __builtin_amdgcn_ballot_w64(hit);
+        while (bits) {
+          const int l = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          const int row = 1 + (e0 + l) / p.r;
+          bool dup = false;
+          for (int x = 0; x < n_fixed; ++x) dup |= fixed[x] == row;
+          if (dup) continue;
+          if (lane == 0) blist[n] = row;
+          ++n;
+        }
       }
+      const bool last = e0 + 64 >= n_entries;
+      if (n >= 64 || last) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        walk(n, true, 0);
+        n = 0;
+      }
+      if (last) break;
     }
   }
-  store_t(p.dk + bh * seq, p.L, k0, c, h, dk);
-  store_t(p.dv + bh * seq, p.L, k0, c, h, dv);
+  if (it.glob && p.chunks > 1) {
+    const int64_t idx = (((int64_t)bh * p.n_grows + it.g) * p.tiles + it.tile) * p.chunks + it.chunk;
+    store_partial(p.ws + (p.n_part + idx) * (kT * kD), c, h, dk);
+    store_partial(p.ws + (2 * p.n_part + idx) * (kT * kD), c, h, dv);
+  } else {
+    store_t(p.dk + bh * seq, p.L, k0, c, h, dk);
+    store_t(p.dv + bh * seq, p.L, k0, c, h, dv);
+  }
+}
+
+// Sum the chunk partials of each global tile (dq, dk, dv) into its bf16
+// rows: one 256-thread workgroup per tile, eight floats per thread.
+__global__ __launch_bounds__(256) void bbsa_bwd_merge(BwdParams p) {
+  const int64_t tiles_per = p.n_part / p.chunks;   // global tiles per gradient
+  const int64_t w = blockIdx.x;
+  const int which = (int)(w / tiles_per);
+  const int64_t t = w % tiles_per;
+  const int tile = (int)(t % p.tiles);
+  const int g = (int)((t / p.tiles) % p.n_grows);
+  const int bh = (int)(t / ((int64_t)p.tiles * p.n_grows));
+  const int blk = p.full ? g : (g == 0 ? 0 : p.nb - 1);
+  const int r = threadIdx.x >> 3, d0 = 8 * (threadIdx.x & 7);
+  const int row = blk * p.block + tile * kT + r;
+  if (row >= p.L) return;
+  const float *base = p.ws + ((int64_t)which * p.n_part + t * p.chunks) * (kT * kD) + r * kD + d0;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int ch = 0; ch < p.chunks; ++ch) {
+    a0 += *(const f32x4 *)(base + (int64_t)ch * (kT * kD));
+    a1 += *(const f32x4 *)(base + (int64_t)ch * (kT * kD) + 4);
+  }
+  bf16_t *out = (which == 0 ? p.dq : which == 1 ? p.dk : p.dv) + (int64_t)bh * p.L * kD + (int64_t)row * kD + d0;
+  *(bf16x4 *)out = __builtin_convertvector(a0, bf16x4);
+  *(bf16x4 *)(out + 4) = __builtin_convertvector(a1, bf16x4);
 }
 
 }  // namespace
@@ -484,19 +682,41 @@ extern "C" int bbsa_backward(const void *q, const void *k, const void *v, const 
   BwdParams p;
   p.q = (const bf16_t *)q; p.k = (const bf16_t *)k; p.v = (const bf16_t *)v; p.o = (const bf16_t *)out;
   p.dout = (const bf16_t *)dout; p.lse = lse; p.mask = mask; p.rand_attn = ln.full ? nullptr : rand_attn;
-  p.delta = delta; p.dq = (bf16_t *)dq; p.dk = (bf16_t *)dk; p.dv = (bf16_t *)dv;
+  p.delta = delta; p.dq = (bf16_t *)dq; p.dk = (bf16_t *)dk; p.dv = (bf16_t *)dv; p.ws = nullptr;
   p.B = B; p.H = H; p.L = L; p.nb = ln.p.nb; p.block = block; p.r = r;
   p.full = ln.full ? 1 : 0;
   p.qk = (ln.p.mode & kModeQK) ? 1 : 0;
   p.tiles = block / kT;
-  const int64_t rows = (int64_t)B * H * L;
-  const int64_t grid = (int64_t)B * H * p.nb * p.tiles;
-  if (grid > 0x7fffffff || (rows + 255) / 256 > 0x7fffffff) return BBSA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(bbsa_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+  p.chunks = (p.nb + kChunkBlocks - 1) / kChunkBlocks;
+  p.n_grows = ln.full ? p.nb : 2;
+  const int64_t bh = (int64_t)B * H;
+  p.lanes = bh >= 8 ? 8 : 1;
+  p.glob_items = p.n_grows * p.tiles * p.chunks;
+  p.mid_items = ln.full ? 0 : (p.nb - 2) * p.tiles;
+  const int64_t pairs_per_lane = (bh + p.lanes - 1) / p.lanes;
+  const int64_t n_glob_lane = pairs_per_lane * p.glob_items;
+  const int64_t grid = p.lanes * (n_glob_lane + pairs_per_lane * p.mid_items);
+  const int64_t rows = bh * L;
+  p.n_part = bh * p.n_grows * p.tiles * p.chunks;
+  if (grid > 0x7fffffff || n_glob_lane > 0x7fffffff || (rows + 31) / 32 > 0x7fffffff ||
+      (int64_t)p.glob_items * pairs_per_lane > 0x7fffffff)
+    return BBSA_ERR_UNSUPPORTED;
+  p.n_glob_lane = (int)n_glob_lane;
+  if (p.chunks > 1) {
+    const int rc = library_workspace((size_t)(3 * p.n_part) * kT * kD * sizeof(float), stream, &p.ws);
+    if (rc != BBSA_OK) return rc;
+  }
+  hipLaunchKernelGGL(bbsa_bwd_delta, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
-  hipLaunchKernelGGL(bbsa_bwd_dq, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  if (mask) hipLaunchKernelGGL(bbsa_bwd_dq<true>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  else hipLaunchKernelGGL(bbsa_bwd_dq<false>, dim3((unsigned)grid), dim3(64), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
-  hipLaunchKernelGGL(bbsa_bwd_dkdv, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  if (p.qk) hipLaunchKernelGGL(bbsa_bwd_dkdv<true>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  else hipLaunchKernelGGL(bbsa_bwd_dkdv<false>, dim3((unsigned)grid), dim3(64), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
+  if (p.chunks > 1) {
+    hipLaunchKernelGGL(bbsa_bwd_merge, dim3((unsigned)(3 * (p.n_part / p.chunks))), dim3(256), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
+  }
   return st;
 }

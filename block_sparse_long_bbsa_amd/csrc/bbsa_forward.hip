@@ -1112,6 +1112,16 @@ int ensure_workspace(size_t bytes, hipStream_t stream, float **ws) {
   return BBSA_OK;
 }
 
+}  // namespace
+
+// The library's per-(device, stream) workspace for other kernels of the
+// library (the backward's split partials), with the same growth rules.
+int bbsa_sched::library_workspace(size_t bytes, hipStream_t stream, float **ws) {
+  return ensure_workspace(bytes, stream, ws);
+}
+
+namespace {
+
 // Enqueue the kernels of a validated call (its workspace pointer set).
 int launch_forward(const Launch &ln, hipStream_t stream, bbsa_dtype dtype, int status) {
   const Params &p = ln.p;

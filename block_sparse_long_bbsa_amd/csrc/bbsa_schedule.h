@@ -18,6 +18,7 @@
 #ifndef BBSA_SCHEDULE_H
 #define BBSA_SCHEDULE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -313,6 +314,10 @@ inline int setup_forward_ex(const void *q, const void *k, const void *v, const f
   launch->full = full;
   return full ? BBSA_OK_FULL_FALLBACK : BBSA_OK;
 }
+
+// The library-owned workspace of the current device and `stream` (see
+// bbsa_forward in bbsa.h), at least `bytes` long.
+int library_workspace(size_t bytes, hipStream_t stream, float **ws);
 
 inline int setup_forward(const void *q, const void *k, const void *v, const float *mask,
                          const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
