@@ -13,17 +13,21 @@
 // forward's row log-sum-exp, so nothing of size L x L is stored.
 //
 // Kernels:
-//   * bbsa_bwd_delta: D per query row (fp32);
 //   * bbsa_bwd_dq: one wavefront per 32-query tile, walking the tile's key
-//     blocks (the forward's list) 32 keys at a time: S^T = K Q^T and
-//     dP^T = V dO^T on MFMA 32x32x16 bf16 (Q and dO in registers, K and V
-//     rows from LDS), dS^T = P^T (dP^T - D) in registers, then
-//     dQ^T += K^T dS^T (K read transposed from LDS);
+//     blocks (the forward's list; a chunk of every block for a global row)
+//     32 keys at a time: S^T = K Q^T and dP^T = V dO^T on MFMA 32x32x16
+//     bf16 (Q and dO in registers, K and V rows from LDS), dS^T = P^T (dP^T
+//     - D) in registers, then dQ^T += K^T dS^T (K read transposed from
+//     LDS).  It also forms D for its rows and stores D and the rows' log2
+//     exponent term for the next kernel;
 //   * bbsa_bwd_dkdv: one wavefront per 32-key tile, walking the query blocks
 //     that attend its key block (global rows, the window, and the rows whose
-//     plan picked it, found by scanning the plan) 32 queries at a time:
-//     S = Q K^T and dP = dO V^T (K and V in registers, Q and dO rows from
-//     LDS), dV^T += dO^T P and dK^T += Q^T dS (Q and dO read transposed).
+//     plan picked it, found by scanning the plan; a chunk of every block for
+//     a global column) 32 queries at a time: S = Q K^T and dP = dO V^T (K
+//     and V in registers, Q and dO rows from LDS), dV^T += dO^T P and
+//     dK^T += Q^T dS (Q and dO read transposed);
+//   * bbsa_bwd_merge: sums the fp32 partials of the split global rows and
+//     columns into their bf16 gradients.
 // Every tile goes from memory to LDS with buffer_load ... lds; the row offset
 // rides in the range-checked per-lane offset, so rows past L read as zeros.
 #include <hip/hip_runtime.h>
@@ -53,10 +57,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPadBias = -10000.0f;
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer: 32-bit format, no swizzle, no stride
 
-// LDS row swizzles (16-byte chunk j of row k sits at chunk j ^ f(k)): R for
-// tiles read by rows (MFMA A operand), T for tiles read transposed.
+// LDS row swizzles (16-byte chunk j of row k sits at chunk j ^ f(k)), with
+// 128-byte rows over 64 four-byte banks.  R, for tiles read only by rows
+// (MFMA A operands): the 16 rows that one row read serves at a time land on
+// 16 distinct chunk positions.  B, for tiles read both by rows and
+// transposed (ds_read_b64_tr_b16): the same property for row reads, and the
+// four rows that each 32-lane half of a transposed read covers sit on eight
+// distinct chunk positions.  B(k + 8) = B(k) ^ 2 and B(k + 16) = B(k).
 __device__ inline int swz_r(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
-__device__ inline int swz_t(int row) { return ((row >> 1) & 1) << 2; }
+__device__ inline int swz_b(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
 __device__ inline int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() & 63; }
 
@@ -68,7 +77,8 @@ struct BwdParams {
   const float *lse;          // [B, H, L]
   const float *mask;         // [B, L] or null
   const int32_t *rand_attn;  // [H, nb-2, r] or null (fallback)
-  float *delta;              // [B, H, L]
+  float *delta;              // [B, H, L]: D = rowsum(dO * out), written by the dq kernel
+  float *rterm;              // [B, H, L]: -(log2e lse - (1 - mq) log2e kPadBias), written by the dq kernel
   bf16_t *dq, *dk, *dv;
   float *ws;                 // split partials of the global rows (dq) and columns (dk, dv)
   int B, H, L, nb, block, r;
@@ -134,12 +144,12 @@ __device__ inline BwdItem decode(const BwdParams &p, int wg) {
 // 8u + l/8 of the tile into LDS position tile + 1024u + 16l.
 struct TileDma {
   int off_r[4];              // source byte offsets within the tile, R swizzle
-  int off_t;                 // T swizzle (the same for the four instructions)
+  int off_b;                 // B swizzle, instructions 0 and 2 (1 and 3: off_b ^ 32)
   __device__ void init(int lane) {
     const int drow = lane >> 3;
 #pragma unroll
     for (int u = 0; u < 4; ++u) off_r[u] = 2 * ((8 * u + drow) * kD + 8 * ((lane & 7) ^ swz_r(8 * u + drow))) - 1024 * u;
-    off_t = 2 * (drow * kD + 8 * ((lane & 7) ^ swz_t(drow)));
+    off_b = 2 * (drow * kD + 8 * ((lane & 7) ^ swz_b(drow)));
   }
 };
 
@@ -150,13 +160,14 @@ constexpr int kNoRow = 1 << 24;
 // Rows row0 .. row0+31 of a [L, 64] bf16 matrix (buffer resource rs) into
 // LDS; rows at or past L read as zeros (the offset is range-checked).  The
 // offsets are 32-bit unsigned: row0 * 128 reaches 2^31 for kNoRow.
-__device__ inline void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, const TileDma &t, int row0, bool tsw) {
+__device__ inline void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, const TileDma &t, int row0, bool bsw) {
   const int base = (int)((unsigned)row0 * (kD * 2));
-  if (tsw) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_t + base, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_t + base, 0, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_t + base, 0, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_t + base, 0, 3072, 0);
+  if (bsw) {
+    const int b0 = t.off_b + base, b1 = (t.off_b ^ 32) + base;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, b0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, b1, 0, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, b0, 0, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, b1, 0, 3072, 0);
   } else {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_r[0] + base, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t *)dst, 16, t.off_r[1] + base, 0, 1024, 0);
@@ -171,24 +182,26 @@ __device__ inline void dma_floats(__amdgpu_buffer_rsrc_t rs, unsigned char *dst,
 }
 
 // A operands of the rows of a tile: row c, d = 16kk + 8h .. +7.
-template <bool TSW>
+template <bool BSW>
 __device__ inline void read_rows(const unsigned char *src, int c, int h, bf16x8 (&a)[4]) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    a[kk] = *(const bf16x8 *)(src + c * 128 + 16 * ((2 * kk + h) ^ (TSW ? swz_t(c) : swz_r(c))));
+    a[kk] = *(const bf16x8 *)(src + c * 128 + 16 * ((2 * kk + h) ^ (BSW ? swz_b(c) : swz_r(c))));
 }
 
-// A operands of the transposed T-swizzled tile X (rows r, columns d): for
+// A operands of the transposed B-swizzled tile X (rows r, columns d): for
 // d-tile dt and row step s, lane (c, h) gets X^T[32dt + c][the row slots
 // 8h .. 8h+7 of step s], in the slot order that the B operands packed by
 // pack_b use (slot 8h + e is row 16s + 4h + (e & 3) + 8 (e >> 2)).
+// toff[dt] addresses rows 0-7 (and 16-23 at +2048); rows 8-15 and 24-31
+// sit at (toff[dt] ^ 32) + 1024 and + 3072, as B(k + 8) = B(k) ^ 2.
 __device__ inline void read_tr(const unsigned char *src, const int (&toff)[2], bf16x8 (&a)[2][2]) {
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + toff[dt] + 2048 * s));
-      const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + toff[dt] + 2048 * s + 1024));
+      const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + (toff[dt] ^ 32) + 2048 * s + 1024));
       a[dt][s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 }
@@ -198,7 +211,7 @@ __device__ inline void tr_offsets(int lane, int (&toff)[2]) {
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt) {
     const int chunk = 4 * dt + 2 * (G & 1) + ((cc & 3) >> 1);
-    toff[dt] = row * 128 + 16 * (chunk ^ swz_t(row)) + 8 * (cc & 1);
+    toff[dt] = row * 128 + 16 * (chunk ^ swz_b(row)) + 8 * (cc & 1);
   }
 }
 
@@ -217,6 +230,14 @@ __device__ inline void pack_b(const f32x16 &x, bf16x8 (&b)[2]) {
 
 __device__ inline f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Flip the sign of every bf16 element (the sign bit of each half).
+__device__ inline void negate(bf16x8 (&x)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    x[kk] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x[kk]) ^ 0x80008000u);
+  }
 }
 __device__ inline f32x16 zero16() {
   f32x16 z;
@@ -272,33 +293,19 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, kBufferWord3);
 }
 
+// LDS slots of the step pipelines: the transfers of step st + kSlots - 1
+// go out while step st computes.
+constexpr int kSlots = 2;
+
 // Wait until at most KEEP vector-memory operations are outstanding: the
-// transfers of the next step (issued for every step, past the end too, as
-// out-of-range transfers of kNoRow), so that this step's have landed.
-// Memory loads complete in issue order.
+// transfers of the steps after this one already issued (issued for every
+// step, past the end too, as out-of-range transfers of kNoRow), so that
+// this step's have landed.  Memory loads complete in issue order.
 template <int KEEP>
 __device__ inline void wait_step() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
 }
 __device__ inline void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// D[t] = sum_e dO[t, e] out[t, e]: eight threads per row, 16 bytes each.
-__global__ __launch_bounds__(256) void bbsa_bwd_delta(BwdParams p) {
-  const int64_t rows = (int64_t)p.B * p.H * p.L;
-  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int part = threadIdx.x & 7;
-  float acc = 0.0f;
-  if (row < rows) {
-    const bf16x8 x = *(const bf16x8 *)(p.dout + row * kD + 8 * part);
-    const bf16x8 y = *(const bf16x8 *)(p.o + row * kD + 8 * part);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (row < rows && part == 0) p.delta[row] = acc;
-}
 
 // Key block of list position t of middle query block i (the forward's list:
 // the two global blocks, the window without them, the plan's blocks).
@@ -314,25 +321,36 @@ __device__ inline int list_block(const BwdParams &p, const int32_t *plan_row, in
 template <int S>
 using SlotId = std::integral_constant<int, S>;
 
-// Runs step(SlotId<st % 3>, st) for st = 0 .. n-1 with the slot as a
-// compile-time constant, so that every LDS access names one of three
+// Runs step(SlotId<st % kSlots>, st) for st = 0 .. n-1 with the slot as a
+// compile-time constant, so that every LDS access names one of the slots'
 // separate arrays and the compiler's own waits for the transfers into LDS
 // wait for the right slot only.
 template <class Step>
 __device__ inline void run_steps(int n, Step &&step) {
   int st = 0;
-  for (; st + 3 <= n; st += 3) {
-    step(SlotId<0>{}, st);
-    step(SlotId<1>{}, st + 1);
-    step(SlotId<2>{}, st + 2);
+  if constexpr (kSlots == 3) {
+    for (; st + 3 <= n; st += 3) {
+      step(SlotId<0>{}, st);
+      step(SlotId<1>{}, st + 1);
+      step(SlotId<2>{}, st + 2);
+    }
+    if (st < n) step(SlotId<0>{}, st);
+    if (st + 1 < n) step(SlotId<1>{}, st + 1);
+  } else {
+    static_assert(kSlots == 2, "two or three slots");
+    for (; st + 2 <= n; st += 2) {
+      step(SlotId<0>{}, st);
+      step(SlotId<1>{}, st + 1);
+    }
+    if (st < n) step(SlotId<0>{}, st);
   }
-  if (st < n) step(SlotId<0>{}, st);
-  if (st + 1 < n) step(SlotId<1>{}, st + 1);
 }
+// Slot of the transfers issued during a step in slot S.
+template <int S>
+using IssueSlot = SlotId<(S + kSlots - 1) % kSlots>;
 
-// dQ: one wavefront per 32-query tile; workgroups of one wavefront.  Three
-// LDS slots, each K (T swizzle) and V (R swizzle) of one step and the key
-// mask: the transfers of step st + 2 go out while step st computes.
+// dQ: one wavefront per 32-query tile; workgroups of one wavefront.  LDS
+// slots, each K (B swizzle) and V (R swizzle) of one step and the key mask.
 template <bool MASKED>
 __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   const BwdItem it = decode(p, (int)blockIdx.x);
@@ -394,7 +412,33 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   const float mq = p.qk ? (qlive ? mask_at(p, mrow, qrow) : 0.0f) : 1.0f;
   const float lse2 =
       qlive ? (p.lse[(int64_t)bh * p.L + qrow] - (p.qk ? kPadBias * (1.0f - mq) : 0.0f)) * kLog2e : 0.0f;
-  const float dlt = qlive ? p.delta[(int64_t)bh * p.L + qrow] : 0.0f;
+  // D of the query row: dO (in registers) against the row of out, lane
+  // (c, h) taking half of row c's columns.  The tile's item (the first
+  // chunk's, for a global row) stores D and -lse2 for the dk/dv kernel.
+  float dlt;
+  {
+    bf16x8 of[4];
+    load_b_rows(p.o + bh * seq, p.L, q0, c, h, of);
+    float acc = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)df[kk][e], (float)of[kk][e], acc);
+    dlt = acc + __shfl_xor(acc, 32);
+    if (qlive && h == 0 && (!it.glob || it.chunk == 0)) {
+      p.delta[(int64_t)bh * p.L + qrow] = dlt;
+      p.rterm[(int64_t)bh * p.L + qrow] = -lse2;
+    }
+  }
+  // The dP^T product runs on -dO from an accumulator holding D, so that it
+  // yields D - dP^T and dS^T = -P^T (D - dP^T) needs no subtraction.
+  negate(df);
+  f32x16 dinit;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dinit[e] = dlt;
+  // The exponent of P in log2 units is s log2e + (1 - m) cpad - lse2 for a
+  // key of mask value m: the bias term is exactly 0 for m = 1.
+  const float cpad = mq * kPadBias * kLog2e;
 
   auto issue = [&](auto S, int st) {
     const int key0 = key_of(st);
@@ -408,44 +452,54 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   // own wait before each slot's reads also counts only that slot's.
   f32x16 dq[2] = {zero16(), zero16()};
   issue(SlotId<0>{}, 0);
-  issue(SlotId<1>{}, 1);
+  if constexpr (kSlots == 3) issue(SlotId<1>{}, 1);
   run_steps(n_steps, [&](auto S, int st) {
-    constexpr int NEXT2 = (decltype(S)::value + 2) % 3;
-    wait_step<kPerStep>();
+    wait_step<(kSlots - 2) * kPerStep>();
     const unsigned char *s = kv(S);
     const int key0 = key_of(st);
     bf16x8 kr[4], vr[4], kt[2][2];
     read_rows<true>(s, c, h, kr);
     read_rows<false>(s + kTile, c, h, vr);
     read_tr(s, toff, kt);
-    f32x4 mkv[4];
+    // x = (1 - m) cpad - lse2 per key; without a mask only keys past L
+    // (the last block of a ragged length) carry the bias.
+    // A step whose 32 keys are all real and unmasked (the common case)
+    // takes x = -lse2 throughout.
+    bool plain;
+    if (MASKED) plain = __builtin_amdgcn_ballot_w64(*(const float *)(mk(S) + 4 * c) != 1.0f) == 0;
+    else plain = key0 + kT <= p.L;
+    // The transfers of step st + kSlots - 1 go into the slot step st - 1 read.
+    issue(IssueSlot<decltype(S)::value>{}, st + kSlots - 1);
+    f32x16 sc = mfma(kr[0], qf[0], zero16());   // S^T[key][query c]
+    f32x16 dp = mfma(vr[0], df[0], dinit);      // D - dP^T[key][query c]
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      if (MASKED) {
-        mkv[jj] = *(const f32x4 *)(mk(S) + 4 * (8 * jj + 4 * h));
-      } else {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) mkv[jj][ii] = key0 + 8 * jj + 4 * h + ii < p.L ? 1.0f : 0.0f;
-      }
-    }
-    // The transfers of step st + 2 go into the slot step st - 1 read.
-    issue(SlotId<NEXT2>{}, st + 2);
-    f32x16 sc = zero16(), dp = zero16();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      sc = mfma(kr[kk], qf[kk], sc);   // S^T[key][query c]
-      dp = mfma(vr[kk], df[kk], dp);   // dP^T[key][query c]
+    for (int kk = 1; kk < 4; ++kk) {
+      sc = mfma(kr[kk], qf[kk], sc);
+      dp = mfma(vr[kk], df[kk], dp);
     }
     // P^T and dS^T; register 4jj + ii is key key0 + 8jj + 4h + ii.
+    if (plain) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+      for (int e = 0; e < 16; ++e) sc[e] = -__builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], kLog2e, -lse2)) * dp[e];
+    } else {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int e = 4 * jj + ii;
-        const float pr =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e] + mq * (kPadBias * (1.0f - mkv[jj][ii])), kLog2e, -lse2));
-        sc[e] = pr * (dp[e] - dlt);
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 xb;
+        if (MASKED) {
+          const f32x4 m = *(const f32x4 *)(mk(S) + 4 * (8 * jj + 4 * h));
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) xb[ii] = __builtin_fmaf(1.0f - m[ii], cpad, -lse2);
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) xb[ii] = key0 + 8 * jj + 4 * h + ii < p.L ? -lse2 : cpad - lse2;
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int e = 4 * jj + ii;
+          sc[e] = -__builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], kLog2e, xb[ii])) * dp[e];
+        }
       }
+    }
     bf16x8 dsb[2];
     pack_b(sc, dsb);
 #pragma unroll
@@ -453,7 +507,7 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) dq[dt] = mfma(kt[dt][ss], dsb[ss], dq[dt]);   // dQ^T[d][query c]
   });
-  wait_all();   // the two transfers past the end
+  wait_all();   // the transfers past the end
   if (it.glob && p.chunks > 1) {
     const int64_t idx = (((int64_t)bh * p.n_grows + it.g) * p.tiles + it.tile) * p.chunks + it.chunk;
     store_partial(p.ws + idx * (kT * kD), c, h, dq);
@@ -466,9 +520,9 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
 // block j: a chunk of every block for a global key block (or on the
 // fallback); else the two global blocks, the window {j-1, j, j+1} (without
 // repeating a global one) and the middle blocks whose plan row picked j,
-// gathered in an LDS list and walked at least 64 blocks at a time.  Three
-// LDS slots, each Q and dO (T swizzle) of one step with the step's lse, D
-// and query mask values.
+// gathered in an LDS list and walked at least 64 blocks at a time.  LDS
+// slots, each Q and dO (B swizzle) of one step with the step's lse, D and
+// query mask values.
 template <bool QK>
 __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
   const BwdItem it = decode(p, (int)blockIdx.x);
@@ -501,7 +555,7 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
   tr_offsets(lane, toff);
   const auto qrs = rsrc(p.q + bh * seq, seq * 2);
   const auto drs = rsrc(p.dout + bh * seq, seq * 2);
-  const auto lrs = rsrc(p.lse + (int64_t)bh * p.L, (int64_t)p.L * 4);
+  const auto lrs = rsrc(p.rterm + (int64_t)bh * p.L, (int64_t)p.L * 4);
   const auto ers = rsrc(p.delta + (int64_t)bh * p.L, (int64_t)p.L * 4);
   const auto mrs = rsrc(mrow, (int64_t)p.L * 4);
 
@@ -510,7 +564,18 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
   bf16x8 kf[4], vf[4];
   load_b_rows(p.k + bh * seq, p.L, k0, c, h, kf);
   load_b_rows(p.v + bh * seq, p.L, k0, c, h, vf);
-  const float kbias = kPadBias * (1.0f - mask_at(p, mrow, k0 + c));
+  // The key column's padding bias in log2 units (exactly 0 for a real,
+  // unmasked key).  The exponent of P is s log2e + rt + x, with rt the
+  // query row's term -(log2e lse - (1 - mq) log2e kPadBias) from the dq
+  // kernel (the lse of a query of mask value mq holds the constant
+  // (1 - mq) kPadBias under query x key masking; mq = 1 otherwise) and
+  // x = kb2 (key-side masking) or mq kb2 (query x key).  A tile whose 32
+  // keys all have kb2 = 0 takes x = 0.
+  const float kb2 = kPadBias * (1.0f - mask_at(p, mrow, k0 + c)) * kLog2e;
+  const bool plain = __builtin_amdgcn_ballot_w64(kb2 != 0.0f) == 0;
+  // The dP product runs on -V from an accumulator holding D (the step's D
+  // values, read from LDS): it yields D - dP, and dS = -P (D - dP).
+  negate(vf);
 
   f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
   constexpr int kPerStep = QK ? 11 : 10;
@@ -532,10 +597,9 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
       if (QK) dma_floats(mrs, vc(S) + 2 * kMaskBytes, row0, lane);
     };
     issue(SlotId<0>{}, 0);
-    issue(SlotId<1>{}, 1);
+    if constexpr (kSlots == 3) issue(SlotId<1>{}, 1);
     run_steps(n_steps, [&](auto S, int st) {
-      constexpr int NEXT2 = (decltype(S)::value + 2) % 3;
-      wait_step<kPerStep>();
+      wait_step<(kSlots - 2) * kPerStep>();
       const unsigned char *s = qd(S);
       const unsigned char *v = vc(S);
       bf16x8 qr[4], dr[4], qt[2][2], dt2[2][2];
@@ -543,34 +607,50 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
       read_rows<true>(s + kTile, c, h, dr);
       read_tr(s, toff, qt);
       read_tr(s + kTile, toff, dt2);
-      // Register 4jj + ii is query row0 + 8jj + 4h + ii; its lse, D and mask
-      // value (rows past L read as 0: their Q and dO are zeros, so they add
-      // nothing).
-      f32x4 ls[4], dl[4], mqv[4];
+      // Register 4jj + ii is query row0 + 8jj + 4h + ii; its row term, D and
+      // mask value (rows past L read as 0: their Q and dO are zeros, so they
+      // add nothing).
+      f32x4 rt[4], dl[4], mqv[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        ls[jj] = *(const f32x4 *)(v + 4 * (8 * jj + 4 * h));
+        rt[jj] = *(const f32x4 *)(v + 4 * (8 * jj + 4 * h));
         dl[jj] = *(const f32x4 *)(v + kMaskBytes + 4 * (8 * jj + 4 * h));
         if (QK) mqv[jj] = *(const f32x4 *)(v + 2 * kMaskBytes + 4 * (8 * jj + 4 * h));
         else mqv[jj] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
       }
-      issue(SlotId<NEXT2>{}, st + 2);
-      f32x16 sc = zero16(), dp = zero16();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        sc = mfma(qr[kk], kf[kk], sc);   // S[query][key c]
-        dp = mfma(dr[kk], vf[kk], dp);   // dP[query][key c]
-      }
+      issue(IssueSlot<decltype(S)::value>{}, st + kSlots - 1);
+      f32x16 dinit;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int e = 4 * jj + ii;
-          const float lse2 = (ls[jj][ii] - (QK ? kPadBias * (1.0f - mqv[jj][ii]) : 0.0f)) * kLog2e;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e] + mqv[jj][ii] * kbias, kLog2e, -lse2));
-          sc[e] = pr;
-          dp[e] = pr * (dp[e] - dl[jj][ii]);
-        }
+        for (int ii = 0; ii < 4; ++ii) dinit[4 * jj + ii] = dl[jj][ii];
+      f32x16 sc = mfma(qr[0], kf[0], zero16());   // S[query][key c]
+      f32x16 dp = mfma(dr[0], vf[0], dinit);      // D - dP[query][key c]
+#pragma unroll
+      for (int kk = 1; kk < 4; ++kk) {
+        sc = mfma(qr[kk], kf[kk], sc);
+        dp = mfma(dr[kk], vf[kk], dp);
+      }
+      if (plain) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int e = 4 * jj + ii;
+            sc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], kLog2e, rt[jj][ii]));
+            dp[e] = -sc[e] * dp[e];
+          }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int e = 4 * jj + ii;
+            const float y = QK ? __builtin_fmaf(mqv[jj][ii], kb2, rt[jj][ii]) : rt[jj][ii] + kb2;
+            sc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], kLog2e, y));
+            dp[e] = -sc[e] * dp[e];
+          }
+      }
       bf16x8 pb[2], db[2];
       pack_b(sc, pb);
       pack_b(dp, db);
@@ -582,7 +662,7 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
           dk[d2] = mfma(qt[d2][ss], db[ss], dk[d2]);    // dK^T[d][key c]
         }
     });
-    wait_all();   // the two transfers past the end
+    wait_all();   // the transfers past the end
   };
 
   if (it.glob) {
@@ -702,12 +782,16 @@ extern "C" int bbsa_backward(const void *q, const void *k, const void *v, const 
       (int64_t)p.glob_items * pairs_per_lane > 0x7fffffff)
     return BBSA_ERR_UNSUPPORTED;
   p.n_glob_lane = (int)n_glob_lane;
-  if (p.chunks > 1) {
-    const int rc = library_workspace((size_t)(3 * p.n_part) * kT * kD * sizeof(float), stream, &p.ws);
+  // Workspace: the row terms, then (with split rows) the partials.
+  {
+    const size_t rt_floats = ((size_t)rows + 63) / 64 * 64;
+    const size_t part_floats = p.chunks > 1 ? (size_t)(3 * p.n_part) * kT * kD : 0;
+    float *ws = nullptr;
+    const int rc = library_workspace((rt_floats + part_floats) * sizeof(float), stream, &ws);
     if (rc != BBSA_OK) return rc;
+    p.rterm = ws;
+    p.ws = ws + rt_floats;
   }
-  hipLaunchKernelGGL(bbsa_bwd_delta, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;
   if (mask) hipLaunchKernelGGL(bbsa_bwd_dq<true>, dim3((unsigned)grid), dim3(64), 0, stream, p);
   else hipLaunchKernelGGL(bbsa_bwd_dq<false>, dim3((unsigned)grid), dim3(64), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return BBSA_ERR_HIP;

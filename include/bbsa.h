@@ -261,12 +261,18 @@ int bbsa_attention_probs(const void *q, const void *k, const float *mask, const 
  * q, k, v, out, dout: device bf16 [B, H, L, d], 16-byte aligned.
  * lse:   device float32 [B, H, L] from bbsa_forward_ex.
  * dq, dk, dv: device bf16 [B, H, L, d], caller-owned, fully overwritten.
- * delta: device float32 [B, H, L], caller-owned scratch the call overwrites
- *        (rowsum(dout * out)).
+ * delta: device float32 [B, H, L], caller-owned, overwritten with
+ *        rowsum(dout * out).
  * mask, rand_attn, shapes, flags: as for bbsa_forward_ex.
  *
  * bf16 only (BBSA_ERR_UNSUPPORTED for BBSA_F32).  Other errors as
- * bbsa_forward_ex.  Enqueues three kernels on `stream`; allocates nothing.
+ * bbsa_forward_ex.  Enqueues two kernels on `stream` (three when the global
+ * rows are split: L > 8 blocks), using the library's workspace for
+ * `stream` (B * H * L floats of row terms, plus fp32 partials of the split
+ * global rows and columns: 3 * B * H * 2 * block * 64 * ceil(nb / 8) floats,
+ * nb = ceil(L / block), or nb in place of 2 on the full-attention fallback);
+ * the workspace grows as bbsa_forward's does, and BBSA_ERR_CAPTURE is
+ * returned if it would have to grow while `stream` is being captured.
  */
 int bbsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
                   const float *lse, const float *mask, const int32_t *rand_attn, int B, int H, int L,

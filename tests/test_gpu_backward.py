@@ -76,6 +76,8 @@ CASES = [
     (1, 2, 704, 64, 3, (650,), False, False, 6),          # short: full attention
     (1, 2, 4096, 64, 3, (3500,), False, False, 7),        # long global rows and columns
     (1, 2, 2048, 64, 12, (2048,), False, False, 8),       # many random blocks per row
+    (1, 2, 512, 64, 3, (480,), False, False, 9),          # full attention, rows not split (8 blocks)
+    (2, 3, 960, 64, 3, (960, 17), True, True, 10),        # ragged, one almost fully padded sequence
 ]
 
 
