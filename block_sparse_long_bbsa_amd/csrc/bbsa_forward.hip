@@ -1017,8 +1017,14 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
   // Each partial's maxima are relative to its padding-bias level: partial c
   // enters with exponent m_c + mq (level_c - top level) * log2(e), where the
   // level difference is exact for 0/1 masks (and 0 on the bf16 path).
-  float top = kInitMax;
-  for (int ch = 0; ch < np; ++ch) top = __builtin_fmaxf(top, base[(int64_t)ch * kPartialFloats + kQT * kD + 2 * kQT]);
+  // bf16 partials all have level 0 (their scores carry the whole bias), so
+  // their merge needs no first pass over the level words.
+  constexpr bool kLevels = sizeof(OutT) != 2;
+  float top = 0.0f;
+  if constexpr (kLevels) {
+    top = kInitMax;
+    for (int ch = 0; ch < np; ++ch) top = __builtin_fmaxf(top, base[(int64_t)ch * kPartialFloats + kQT * kD + 2 * kQT]);
+  }
   // One pass, kMergeBatch chunks at a time: all loads of a batch are issued
   // before any of them is used; the running (M, den, acc) is rescaled when a
   // batch raises the maximum.
@@ -1031,7 +1037,7 @@ __global__ __launch_bounds__(64) void bbsa_combine(Params p) {
     for (int u = 0; u < kMergeBatch; ++u) {
       const int ch = min(c0 + u, np - 1);   // repeats stay unused
       const float *part = base + (int64_t)ch * kPartialFloats;
-      mc[u] = part[kQT * kD + q] + mq * (part[kQT * kD + 2 * kQT] - top) * kLog2e;
+      mc[u] = kLevels ? part[kQT * kD + q] + mq * (part[kQT * kD + 2 * kQT] - top) * kLog2e : part[kQT * kD + q];
       lc[u] = part[kQT * kD + kQT + q];
       oc[u] = *(const f32x4 *)(part + q * kD + 4 * dq);
     }
