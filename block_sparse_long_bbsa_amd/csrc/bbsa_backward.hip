@@ -32,6 +32,7 @@
 // rides in the range-checked per-lane offset, so rows past L read as zeros.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
@@ -69,7 +70,11 @@ __device__ inline int swz_b(int row) { return (((row >> 1) & 1) << 2) | ((row >>
 
 __device__ inline int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() & 63; }
 
-constexpr int kChunkBlocks = 8;                 // blocks per chunk of a global row or column
+// A global row or column is walked in chunks of about kChunkBlocks blocks,
+// and in at least two: fewer, longer chunks leave fewer partials to merge,
+// and two halves keep the global items from forming the tail (at nb = 64 two
+// chunks beat one, four and eight; at nb = 256 four beat eight and sixteen).
+constexpr int kChunkBlocks = 64;
 constexpr int kMaskBytes = 256;                 // per-step array of 64 floats (lanes 32..63 repeat 0..31)
 
 struct BwdParams {
@@ -767,7 +772,7 @@ extern "C" int bbsa_backward(const void *q, const void *k, const void *v, const 
   p.full = ln.full ? 1 : 0;
   p.qk = (ln.p.mode & kModeQK) ? 1 : 0;
   p.tiles = block / kT;
-  p.chunks = (p.nb + kChunkBlocks - 1) / kChunkBlocks;
+  p.chunks = std::max(std::min(p.nb, 2), (p.nb + kChunkBlocks - 1) / kChunkBlocks);
   p.n_grows = ln.full ? p.nb : 2;
   const int64_t bh = (int64_t)B * H;
   p.lanes = bh >= 8 ? 8 : 1;

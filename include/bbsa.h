@@ -266,11 +266,12 @@ int bbsa_attention_probs(const void *q, const void *k, const float *mask, const 
  * mask, rand_attn, shapes, flags: as for bbsa_forward_ex.
  *
  * bf16 only (BBSA_ERR_UNSUPPORTED for BBSA_F32).  Other errors as
- * bbsa_forward_ex.  Enqueues two kernels on `stream` (three when the global
- * rows are split: L > 8 blocks), using the library's workspace for
- * `stream` (B * H * L floats of row terms, plus fp32 partials of the split
- * global rows and columns: 3 * B * H * 2 * block * 64 * ceil(nb / 8) floats,
- * nb = ceil(L / block), or nb in place of 2 on the full-attention fallback);
+ * bbsa_forward_ex.  Enqueues three kernels on `stream` (two when nb = 1),
+ * using the library's workspace for `stream` (B * H * L floats of row
+ * terms, plus fp32 partials of the split global rows and columns:
+ * 3 * B * H * 2 * block * 64 * c floats with nb = ceil(L / block) and
+ * c = max(min(nb, 2), ceil(nb / 64)) chunks per row, or nb in place of 2 on
+ * the full-attention fallback);
  * the workspace grows as bbsa_forward's does, and BBSA_ERR_CAPTURE is
  * returned if it would have to grow while `stream` is being captured.
  */
