@@ -126,3 +126,35 @@ def test_backward_refuses_fp32():
     ra = torch.from_numpy(bbsa.bbsa_plan_rand_attn(1, 16, 3, 0)).cuda()
     with pytest.raises(ValueError):
         bbsa.bbsa_backward(q, q, q, q, q, lse, None, ra, 64, 3)
+
+
+def test_backward_on_two_streams_at_once():
+    # Two backward calls that both need the workspace (split global rows),
+    # enqueued on two streams without ordering between them: each stream has
+    # its own workspace, so both equal their calls made one at a time.
+    announce("backward two streams")
+    runs = []
+    for seed in (41, 42):
+        inp = workloads.make_case(1, 2, 4096, 64, seed, valid=(4000,))
+        cplan, _ = plans(2, 64, 3, seed)
+        q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+        mask = to_dev(inp["mask"], torch.float32)
+        ra = torch.from_numpy(cplan).cuda()
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+        out, lse, _ = bbsa.bbsa_forward_ex(q, k, v, mask, ra, 64, 3, return_lse=True)
+        alone = bbsa.bbsa_backward(q, k, v, out, dout, lse, mask, ra, 64, 3)
+        torch.cuda.synchronize()
+        runs.append(((q, k, v, out, dout, lse, mask, ra), [t.float().cpu().numpy() for t in alone[:3]]))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    results = []
+    for s, (args, _) in zip(streams, runs):
+        with torch.cuda.stream(s):
+            results.append(bbsa.bbsa_backward(*args, 64, 3))
+    torch.cuda.synchronize()
+    for (_, alone), got in zip(runs, results):
+        assert got[3] == bbsa.BBSA_OK
+        for name, t, a in zip(("dq", "dk", "dv"), got[:3], alone):
+            assert np.array_equal(t.float().cpu().numpy(), a), f"{name} differs from the call made alone"

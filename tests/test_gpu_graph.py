@@ -73,6 +73,52 @@ def test_graph_replay_matches_eager(B, H, L, block, r, dtype):
     assert_close(gather_rows(got.astype(np.float64), blocks, block), want, dtype, "graph replay vs oracle")
 
 
+@pytest.mark.parametrize("B,H,L,block,r,qk", [
+    (2, 2, 4096, 64, 3, False),     # global rows and columns split: workspace partials + merge kernel
+    (1, 2, 2048, 128, 2, True),     # block 128, query x key masking
+])
+def test_backward_graph_replay_matches_eager(B, H, L, block, r, qk):
+    # The backward keeps its row terms and partials in the stream's library
+    # workspace; after an eager call has sized it, a captured call allocates
+    # nothing and every replay equals the eager call bit for bit.
+    announce(f"backward graph B{B} H{H} L{L} block{block} r{r} qk={qk}")
+    seed = 37
+    inp = workloads.make_case(B, H, L, 64, seed, valid=[L - 300 * i for i in range(B)])
+    nb = L // block
+    cplan, _ = plans(H, nb, r, seed)
+    q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    mask = to_dev(inp["mask"], torch.float32)
+    ra = torch.from_numpy(cplan).cuda()
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    out, lse, st = bbsa.bbsa_forward_ex(q, k, v, mask, ra, block, r, return_lse=True, query_key_mask=qk)
+    assert st == bbsa.BBSA_OK
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):
+        eager = bbsa.bbsa_backward(q, k, v, out, dout, lse, mask, ra, block, r, query_key_mask=qk)
+    assert eager[3] == bbsa.BBSA_OK
+    torch.cuda.synchronize()
+    eager = [t.float().cpu().numpy() for t in eager[:3]]
+
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty_like(lse)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        st_cap = bbsa.bbsa_backward(q, k, v, out, dout, lse, mask, ra, block, r, dq=dq, dk=dk, dv=dv,
+                                    delta=delta, query_key_mask=qk)[3]
+    assert st_cap == bbsa.BBSA_OK
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))    # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("dq", "dk", "dv"), (dq, dk, dv), eager):
+            assert np.array_equal(t.float().cpu().numpy(), e), f"replay {rep}: {name} differs from the eager call"
+
+
 def _hip():
     import ctypes
     h = ctypes.CDLL("libamdhip64.so")
