@@ -73,7 +73,7 @@ __device__ inline int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() &
 // A global row or column is walked in chunks of about kChunkBlocks blocks,
 // and in at least two: fewer, longer chunks leave fewer partials to merge,
 // and two halves keep the global items from forming the tail (at nb = 64 two
-// chunks beat one, four and eight; at nb = 256 four beat eight and sixteen).
+// chunks beat one, four and eight; at nb = 256 four beat eight and 32).
 constexpr int kChunkBlocks = 64;
 constexpr int kMaskBytes = 256;                 // per-step array of 64 floats (lanes 32..63 repeat 0..31)
 
