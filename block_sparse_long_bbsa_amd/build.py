@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbbsa.so")
 
-SOURCES = ["bbsa_forward.hip", "bbsa_probs.hip", "bbsa_backward.hip", "bbsa_plan.cpp", "bbsa_host.cpp"]
+SOURCES = ["bbsa_forward.hip", "bbsa_probs.hip", "bbsa_backward.hip", "bbsa_backward_f32.hip", "bbsa_plan.cpp",
+           "bbsa_host.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

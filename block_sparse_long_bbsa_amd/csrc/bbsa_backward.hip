@@ -763,7 +763,11 @@ extern "C" int bbsa_backward(const void *q, const void *k, const void *v, const 
   auto misaligned = [](const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) != 0; };
   if (misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(delta, 4))
     return BBSA_ERR_ARG;
-  if (dtype != BBSA_BF16) return BBSA_ERR_UNSUPPORTED;
+  if (dtype == BBSA_F32) {
+    const int rc = launch_backward_f32(q, k, v, out, dout, mask, ln.full ? nullptr : rand_attn, B, H, L, ln.p.nb,
+                                       block, r, ln.full, (ln.p.mode & kModeQK) != 0, dq, dk, dv, delta, stream);
+    return rc < 0 ? rc : st;
+  }
   BwdParams p;
   p.q = (const bf16_t *)q; p.k = (const bf16_t *)k; p.v = (const bf16_t *)v; p.o = (const bf16_t *)out;
   p.dout = (const bf16_t *)dout; p.lse = lse; p.mask = mask; p.rand_attn = ln.full ? nullptr : rand_attn;

@@ -319,6 +319,13 @@ inline int setup_forward_ex(const void *q, const void *k, const void *v, const f
 // bbsa_forward in bbsa.h), at least `bytes` long.
 int library_workspace(size_t bytes, hipStream_t stream, float **ws);
 
+// The fp32 backward's kernels (csrc/bbsa_backward_f32.hip), launched by
+// bbsa_backward after its argument checks; nb is the padded block count.
+int launch_backward_f32(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                        const float *mask, const int32_t *rand_attn, int B, int H, int L, int nb, int block,
+                        int r, bool full, bool qk, void *dq, void *dk, void *dv, float *delta,
+                        hipStream_t stream);
+
 inline int setup_forward(const void *q, const void *k, const void *v, const float *mask,
                          const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
                          void *out, int dtype, Launch *launch) {

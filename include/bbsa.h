@@ -258,22 +258,27 @@ int bbsa_attention_probs(const void *q, const void *k, const float *mask, const 
  * forward must have been run with the same arguments and flags and its
  * `out` and `lse` passed here.
  *
- * q, k, v, out, dout: device bf16 [B, H, L, d], 16-byte aligned.
+ * q, k, v, out, dout: device [B, H, L, d] of `dtype`, 16-byte aligned.
  * lse:   device float32 [B, H, L] from bbsa_forward_ex.
- * dq, dk, dv: device bf16 [B, H, L, d], caller-owned, fully overwritten.
+ * dq, dk, dv: device [B, H, L, d] of `dtype`, caller-owned, fully
+ *        overwritten.
  * delta: device float32 [B, H, L], caller-owned, overwritten with
  *        rowsum(dout * out).
  * mask, rand_attn, shapes, flags: as for bbsa_forward_ex.
  *
- * bf16 only (BBSA_ERR_UNSUPPORTED for BBSA_F32).  Other errors as
- * bbsa_forward_ex.  Enqueues three kernels on `stream` (two when nb = 1),
+ * BBSA_BF16: MFMA kernels; three kernels on `stream` (two when nb = 1),
  * using the library's workspace for `stream` (B * H * L floats of row
  * terms, plus fp32 partials of the split global rows and columns:
  * 3 * B * H * 2 * block * 64 * c floats with nb = ceil(L / block) and
  * c = max(min(nb, 2), ceil(nb / 64)) chunks per row, or nb in place of 2 on
- * the full-attention fallback);
- * the workspace grows as bbsa_forward's does, and BBSA_ERR_CAPTURE is
- * returned if it would have to grow while `stream` is being captured.
+ * the full-attention fallback).
+ * BBSA_F32: an fp32 path on the vector units (three kernels; workspace
+ * 2 * B * H * L floats), which recomputes each row's normaliser relative to
+ * its padding-bias level as the fp32 forward does, so rows whose keys all
+ * share one mask value keep fp32 precision; `lse` is checked but not read.
+ * Errors as bbsa_forward_ex.  The workspace grows as bbsa_forward's does,
+ * and BBSA_ERR_CAPTURE is returned if it would have to grow while `stream`
+ * is being captured.
  */
 int bbsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
                   const float *lse, const float *mask, const int32_t *rand_attn, int B, int H, int L,

@@ -1,18 +1,24 @@
-"""Parity of the bf16 backward (bbsa_backward) with the oracle's float64
+"""Parity of the backward (bbsa_backward) with the oracle's float64
 gradients on MI355X ("models 仓库中的 BigBird…", section "梯度检查点的实现方式";
 "BigBirdPegasus…", section "使用限制与注意事项").
 
-The GPU path runs bbsa_forward_ex (bf16 output and fp32 row log-sum-exp),
-then bbsa_backward; the oracle differentiates the float64 definition at the
-same bf16 inputs and output gradient.
+The GPU path runs bbsa_forward_ex (output and fp32 row log-sum-exp), then
+bbsa_backward; the oracle differentiates the float64 definition at the same
+inputs (bf16-exact for the bf16 path) and output gradient.
 
-Tolerance (derived from the arithmetic, for each of dq, dk, dv with s the
-largest magnitude of the oracle's gradient, at least 1): max abs <= 2e-2 s
-and mean abs <= 2e-3 s.  The GPU path's errors are relative to the
-gradient's scale: P carries the forward lse's error (the bf16 path sums
-bf16-rounded probabilities: up to 2^-9 relative), rowsum(dout * out) uses
-the forward's bf16 output (2^-9 relative per element), and ds and p are
-rounded to bf16 (2^-9) before the products that accumulate them in fp32.
+Tolerances, for each of dq, dk, dv with s the largest magnitude of the
+oracle's gradient (at least 1):
+- bf16: max abs <= 2e-2 s and mean abs <= 2e-3 s.  The GPU path's errors
+  are relative to the gradient's scale: P carries the forward lse's error
+  (the bf16 path sums bf16-rounded probabilities: up to 2^-9 relative),
+  rowsum(dout * out) uses the forward's bf16 output (2^-9 relative per
+  element), and ds and p are rounded to bf16 (2^-9) before the products
+  that accumulate them in fp32.
+- fp32: max abs <= 1e-4 s and mean abs <= 1e-5 s.  Everything is fp32: the
+  forward output (relative error ~1e-6), the 64-term dot products and the
+  sums over up to L keys (each ~1e-6 relative), and the exponentials (a few
+  ulps); the row normaliser is recomputed relative to the row's bias level,
+  so no -10000 cancellation enters.
 """
 import numpy as np
 import pytest
@@ -24,8 +30,8 @@ from gpu_helpers import PARITY_LOG, announce, plans, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MAX_REL = 2e-2
-MEAN_REL = 2e-3
+MAX_REL = {"bf16": 2e-2, "f32": 1e-4}
+MEAN_REL = {"bf16": 2e-3, "f32": 1e-5}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -39,8 +45,9 @@ def bf16_exact(x):
     return workloads.round_to_bf16(x)
 
 
-def run_backward(inp, dout, block, r, plan, pad=False, qk=False):
-    q, k, v, do = (to_dev(x, torch.bfloat16) for x in (inp["q"], inp["k"], inp["v"], dout))
+def run_backward(inp, dout, block, r, plan, pad=False, qk=False, dtype="bf16"):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, do = (to_dev(x, tdt) for x in (inp["q"], inp["k"], inp["v"], dout))
     mask = to_dev(inp["mask"], torch.float32)
     ra = torch.from_numpy(plan).cuda() if plan is not None else None
     out, lse, st = bbsa.bbsa_forward_ex(q, k, v, mask, ra, block, r, return_lse=True, pad_to_block=pad,
@@ -55,15 +62,15 @@ def run_backward(inp, dout, block, r, plan, pad=False, qk=False):
     return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)], st
 
 
-def check(got, want, what):
+def check(got, want, what, dtype="bf16"):
     for name, g, w in zip(("dq", "dk", "dv"), got, want):
         assert np.isfinite(g).all(), f"{what} {name}: non-finite (unwritten?) entries"
         s = max(1.0, float(np.abs(w).max()))
         err = np.abs(g - w)
         announce(f"{what} {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} scale={s:.3g}")
         PARITY_LOG.append((f"{what} {name}", int(np.prod(g.shape[:-1])), float(err.max()), float(err.mean())))
-        assert err.max() <= MAX_REL * s, f"{what} {name}: max abs {err.max()} (scale {s})"
-        assert err.mean() <= MEAN_REL * s, f"{what} {name}: mean abs {err.mean()} (scale {s})"
+        assert err.max() <= MAX_REL[dtype] * s, f"{what} {name}: max abs {err.max()} (scale {s})"
+        assert err.mean() <= MEAN_REL[dtype] * s, f"{what} {name}: mean abs {err.mean()} (scale {s})"
 
 
 CASES = [
@@ -120,12 +127,31 @@ def test_backward_bigbird_base_workload():
         check([g[sl] for g in got], want, f"backward {w.name} pair {bh}")
 
 
-def test_backward_refuses_fp32():
-    q = torch.zeros((1, 1, 1024, 64), dtype=torch.float32, device="cuda")
-    lse = torch.zeros((1, 1, 1024), dtype=torch.float32, device="cuda")
-    ra = torch.from_numpy(bbsa.bbsa_plan_rand_attn(1, 16, 3, 0)).cuda()
-    with pytest.raises(ValueError):
-        bbsa.bbsa_backward(q, q, q, q, q, lse, None, ra, 64, 3)
+F32_CASES = [
+    # B, H, L, block, r, valid, pad, qk, seed
+    (1, 2, 1024, 64, 3, (1024,), False, False, 21),       # the fp32 workload's shape
+    (2, 2, 1024, 64, 3, (1024, 0), False, False, 22),     # a fully padded sequence
+    (2, 2, 1536, 64, 3, (1536, 900), False, True, 23),    # query x key
+    (1, 2, 1000, 64, 3, (937,), True, False, 24),         # ragged length
+    (1, 2, 2048, 128, 2, (1900,), False, False, 25),      # block 128
+    (1, 2, 704, 64, 3, (650,), False, False, 26),         # short: full attention
+]
+
+
+@pytest.mark.parametrize("B,H,L,block,r,valid,pad,qk,seed", F32_CASES)
+def test_backward_f32_matches_oracle(B, H, L, block, r, valid, pad, qk, seed):
+    announce(f"backward f32 B{B} H{H} L{L} block{block} r{r} valid={valid} pad={pad} qk={qk}")
+    inp = workloads.make_case(B, H, L, 64, 200 + seed, dtype="f32", valid=valid)
+    rng = np.random.Generator(np.random.PCG64(300 + seed))
+    dout = rng.standard_normal((B, H, L, 64)).astype(np.float32)
+    nb = -(-L // block)
+    full = L <= (5 + 2 * r) * block
+    cplan, oplan = (None, None) if nb < 5 + r else plans(H, nb, r, seed)
+    got, st = run_backward(inp, dout, block, r, None if full else cplan, pad=pad, qk=qk, dtype="f32")
+    assert st == (bbsa.BBSA_OK_FULL_FALLBACK if full else bbsa.BBSA_OK)
+    f = oracle.backward_padded if pad else oracle.backward
+    want = f(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block, dout, query_key_mask=qk)
+    check(got, want, f"backward f32 L{L} pad={pad} qk={qk}", dtype="f32")
 
 
 def test_backward_on_two_streams_at_once():
