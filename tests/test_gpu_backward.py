@@ -45,10 +45,10 @@ def bf16_exact(x):
     return workloads.round_to_bf16(x)
 
 
-def run_backward(inp, dout, block, r, plan, pad=False, qk=False, dtype="bf16"):
+def run_backward(inp, dout, block, r, plan, pad=False, qk=False, dtype="bf16", no_mask=False):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     q, k, v, do = (to_dev(x, tdt) for x in (inp["q"], inp["k"], inp["v"], dout))
-    mask = to_dev(inp["mask"], torch.float32)
+    mask = None if no_mask else to_dev(inp["mask"], torch.float32)
     ra = torch.from_numpy(plan).cuda() if plan is not None else None
     out, lse, st = bbsa.bbsa_forward_ex(q, k, v, mask, ra, block, r, return_lse=True, pad_to_block=pad,
                                         query_key_mask=qk, warn_fallback=False)
@@ -86,6 +86,7 @@ CASES = [
     (1, 2, 512, 64, 3, (480,), False, False, 9),          # full attention, 8 blocks in two chunks
     (1, 2, 64, 64, 3, (50,), False, False, 11),           # one block: rows not split, no merge
     (2, 3, 960, 64, 3, (960, 17), True, True, 10),        # ragged, one almost fully padded sequence
+    (2, 2, 1024, 64, 3, (1024, 0), False, False, 12),     # a fully padded sequence
 ]
 
 
@@ -184,3 +185,24 @@ def test_backward_on_two_streams_at_once():
         assert got[3] == bbsa.BBSA_OK
         for name, t, a in zip(("dq", "dk", "dv"), got[:3], alone):
             assert np.array_equal(t.float().cpu().numpy(), a), f"{name} differs from the call made alone"
+
+
+@pytest.mark.parametrize("L,block,pad,dtype", [(2048, 64, False, "bf16"), (1000, 64, True, "bf16"),
+                                               (2048, 128, False, "bf16"), (1000, 64, True, "f32")])
+def test_backward_without_mask(L, block, pad, dtype):
+    # A NULL mask: every real key is unmasked; with a ragged length only the
+    # positions past L carry the padding bias.
+    announce(f"backward no mask L{L} block{block} pad={pad} {dtype}")
+    B, H, r, seed = 1, 2, 3, 13
+    inp = workloads.make_case(B, H, L, 64, 200 + seed, dtype=dtype)
+    rng = np.random.Generator(np.random.PCG64(300 + seed))
+    dout = rng.standard_normal((B, H, L, 64)).astype(np.float32)
+    if dtype == "bf16":
+        dout = bf16_exact(dout)
+    nb = -(-L // block)
+    cplan, oplan = plans(H, nb, r, seed)
+    got, st = run_backward(inp, dout, block, r, cplan, pad=pad, dtype=dtype, no_mask=True)
+    assert st == bbsa.BBSA_OK
+    f = oracle.backward_padded if pad else oracle.backward
+    want = f(inp["q"], inp["k"], inp["v"], None, oplan, block, dout)
+    check(got, want, f"backward no mask L{L} pad={pad}", dtype=dtype)
