@@ -62,6 +62,16 @@ def run_backward(inp, dout, block, r, plan, pad=False, qk=False, dtype="bf16", n
     return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)], st
 
 
+def plans_for(H, nb, r, seed, full):
+    """(C plan, oracle plan).  With fewer than 5 + r blocks no plan exists and
+    the call is the full-attention fallback; the oracle takes that decision
+    from the plan's shape (its r), so it gets a placeholder of that shape."""
+    if nb >= 5 + r:
+        return plans(H, nb, r, seed)
+    assert full
+    return None, np.zeros((H, max(nb - 2, 0), r), dtype=np.int32)
+
+
 def check(got, want, what, dtype="bf16"):
     for name, g, w in zip(("dq", "dk", "dv"), got, want):
         assert np.isfinite(g).all(), f"{what} {name}: non-finite (unwritten?) entries"
@@ -98,7 +108,7 @@ def test_backward_matches_oracle(B, H, L, block, r, valid, pad, qk, seed):
     dout = bf16_exact(rng.standard_normal((B, H, L, 64)).astype(np.float32))
     nb = -(-L // block)
     full = L <= (5 + 2 * r) * block
-    cplan, oplan = (None, None) if nb < 5 + r else plans(H, nb, r, seed)
+    cplan, oplan = plans_for(H, nb, r, seed, full)
     got, st = run_backward(inp, dout, block, r, None if full else cplan, pad=pad, qk=qk)
     assert st == (bbsa.BBSA_OK_FULL_FALLBACK if full else bbsa.BBSA_OK)
     f = oracle.backward_padded if pad else oracle.backward
@@ -147,7 +157,7 @@ def test_backward_f32_matches_oracle(B, H, L, block, r, valid, pad, qk, seed):
     dout = rng.standard_normal((B, H, L, 64)).astype(np.float32)
     nb = -(-L // block)
     full = L <= (5 + 2 * r) * block
-    cplan, oplan = (None, None) if nb < 5 + r else plans(H, nb, r, seed)
+    cplan, oplan = plans_for(H, nb, r, seed, full)
     got, st = run_backward(inp, dout, block, r, None if full else cplan, pad=pad, qk=qk, dtype="f32")
     assert st == (bbsa.BBSA_OK_FULL_FALLBACK if full else bbsa.BBSA_OK)
     f = oracle.backward_padded if pad else oracle.backward
@@ -206,3 +216,43 @@ def test_backward_without_mask(L, block, pad, dtype):
     f = oracle.backward_padded if pad else oracle.backward
     want = f(inp["q"], inp["k"], inp["v"], None, oplan, block, dout)
     check(got, want, f"backward no mask L{L} pad={pad}", dtype=dtype)
+
+
+def draw_backward_case(i):
+    rng = np.random.Generator(np.random.PCG64(9100 + i))
+    block = int(rng.choice([64, 128]))
+    r = int(rng.integers(1, 6))
+    nb = int(rng.integers(1, max(2, 2048 // block) + 1))
+    L = nb * block
+    pad = bool(i % 2 == 1 and L > block)
+    if pad:
+        L -= int(rng.integers(1, block))
+    B = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 4))
+    dtype = "f32" if i % 3 == 2 else "bf16"
+    valid = [int(rng.integers(0, L + 1)) for _ in range(B)] if rng.random() < 0.7 else None
+    qk = bool(valid is not None and rng.random() < 0.4)
+    q_scale = float(rng.choice([1.0 / 8.0, 0.5, 1.0]))
+    return B, H, L, block, r, pad, dtype, valid, qk, q_scale
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_backward_seeded_sweep(i):
+    # Seeded draws of shape, block, r, ragged length, dtype, padding, query x
+    # key mode and score scale (every case reproducible from its index).
+    B, H, L, block, r, pad, dtype, valid, qk, q_scale = draw_backward_case(i)
+    announce(f"backward sweep {i}: B{B} H{H} L{L} block{block} r{r} pad={pad} {dtype} valid={valid} "
+             f"qk={qk} q_scale={q_scale}")
+    inp = workloads.make_case(B, H, L, 64, 9100 + i, dtype=dtype, valid=valid, q_scale=q_scale)
+    rng = np.random.Generator(np.random.PCG64(9200 + i))
+    dout = rng.standard_normal((B, H, L, 64)).astype(np.float32)
+    if dtype == "bf16":
+        dout = bf16_exact(dout)
+    nb = -(-L // block)
+    full = L <= (5 + 2 * r) * block
+    cplan, oplan = plans_for(H, nb, r, 9100 + i, full)
+    got, st = run_backward(inp, dout, block, r, None if full else cplan, pad=pad, qk=qk, dtype=dtype)
+    assert st == (bbsa.BBSA_OK_FULL_FALLBACK if full else bbsa.BBSA_OK)
+    f = oracle.backward_padded if pad else oracle.backward
+    want = f(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, block, dout, query_key_mask=qk)
+    check(got, want, f"backward sweep {i}", dtype=dtype)
