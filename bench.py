@@ -159,6 +159,41 @@ def roofline(w, step_ms):
     return rec, flops, nbytes
 
 
+def executed_pair_fraction(w, mask, plan, bbsa) -> float:
+    """Share of the pattern's (64-row query tile, key block) pairs that the
+    bf16 kernels execute for this workload's mask: a tile leaves out the key
+    blocks whose mask values are all 0 when its list (the kernels' own lists,
+    from the library's work map) holds a key of mask 1, except the block at
+    list position 0.  The useful flops above count every pattern pair,
+    padding included; this is for reporting the work actually done."""
+    if w.dtype != "bf16":
+        return 1.0
+    st, _, rec = bbsa.bbsa_work_map(w.B, w.H, w.L, w.d, w.block, w.r, bbsa.BBSA_BF16, plan)
+    if st < 0 or len(rec) == 0:
+        return 1.0
+    blocks = mask.reshape(w.B, w.nb, w.block)
+    padded = (blocks == 0).all(axis=2)          # [B, nb]
+    has_one = (blocks == 1).any(axis=2)         # [B, nb]
+    total = executed = 0
+    for row in rec:
+        b = int(row[3]) // w.H
+        lst = row[16 + row[8]:16 + row[9]]
+        n = len(lst)
+        total += n
+        if has_one[b, lst].any():
+            executed += n - int(padded[b, lst[1:]].sum())
+        else:
+            executed += n
+    return executed / total if total else 1.0
+
+
+def add_executed(roof, frac):
+    """The executed share of the pattern pairs and the MFMA fraction of the
+    work actually done (the fractions above count every pattern pair)."""
+    roof["executed_pair_fraction"] = round(frac, 4)
+    roof["executed_mfma_frac"] = round(roof["mfma_frac"] * frac, 4)
+
+
 class Runner:
     """Device copies of one workload's inputs and the step that runs on them."""
 
@@ -338,6 +373,7 @@ def main():
     roof, flops, nbytes = roofline(w, ms)
     roof["traffic"] = read_traffic(w.name)
     roof["kernel"] = "bbsa_attn_bf16" if w.dtype == "bf16" else "bbsa_attn_f32"
+    add_executed(roof, executed_pair_fraction(w, run.inp["mask"], run.plan, bbsa))
     # The step is one attention-kernel launch (plus the merge kernel only for
     # rows longer than 4096 keys), so the average launch duration over the
     # timed region is the step time; per-launch events (which add their own
@@ -368,6 +404,7 @@ def main():
         r2.preroll(args.preroll)
         ms2 = r2.timed(args.steps, args.warmup)
         rf2, fl2, nb2 = roofline(r2.w, ms2)
+        add_executed(rf2, executed_pair_fraction(r2.w, r2.inp["mask"], r2.plan, bbsa))
         v2 = fl2 / (ms2 * 1e-3) / 1e12
         log(f"{r2.w.name}: step {ms2 * 1e3:.2f} us; {v2:.1f} useful TFLOP/s; frac {rf2['frac']} "
             f"({rf2['bound']}); MFMA {rf2['mfma_frac']} HBM {rf2['hbm_frac']}")

@@ -28,6 +28,7 @@ BBSA_ERR_SCRATCH = -7
 
 BBSA_FLAG_PAD_TO_BLOCK = 1
 BBSA_FLAG_QUERY_KEY_MASK = 2
+BBSA_FLAG_KEEP_PADDED_BLOCKS = 4
 
 WORK_RECORD_INTS = 80
 
@@ -234,14 +235,17 @@ def bbsa_forward(q, k, v, mask, rand_attn, block: int, r: int, out=None, stream=
 
 def bbsa_forward_ex(q, k, v, mask, rand_attn, block: int, r: int, out=None, lse=None, stream=None,
                     pad_to_block: bool = False, query_key_mask: bool = False, return_lse: bool = False,
-                    warn_fallback: bool = True):
+                    warn_fallback: bool = True, keep_padded_blocks: bool = False):
     """``bbsa_forward`` with options (see include/bbsa.h):
 
     pad_to_block: L need not be a multiple of ``block`` (the sequence is
     handled as padded to ceil(L/block) blocks; rand_attn is the plan of that
     block count).  query_key_mask: bias -10000 (1 - m[query] m[key]).
-    return_lse / lse: also produce the float32 ``[B, H, L]`` row
-    log-sum-exp.  Returns ``(out, status)`` or ``(out, lse, status)``.
+    keep_padded_blocks: also compute key blocks whose keys all have mask 0
+    (by default a tile that attends a key of mask 1 leaves them out, which
+    does not change the result).  return_lse / lse: also produce the float32
+    ``[B, H, L]`` row log-sum-exp.  Returns ``(out, status)`` or
+    ``(out, lse, status)``.
     """
     import torch
     if out is None:
@@ -253,7 +257,8 @@ def bbsa_forward_ex(q, k, v, mask, rand_attn, block: int, r: int, out=None, lse=
         if not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous float32 [B, H, L] GPU tensor")
     args = list(_marshal(q, k, v, mask, rand_attn, block, r, out, stream, pad=pad_to_block))
-    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0)
+    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0) | \
+        (BBSA_FLAG_KEEP_PADDED_BLOCKS if keep_padded_blocks else 0)
     cargs = args[:12] + [None if lse is None else lse.data_ptr(), args[12], args[13], flags]
     with torch.cuda.device(q.device):
         st = lib().bbsa_forward_ex(*cargs)

@@ -32,7 +32,11 @@
 //     (O, max, sum) in LDS with the log-sum-exp rule, and longer rows (and
 //     the fp32 path) leave partials in a workspace for a second kernel;
 //   * workgroups are mapped onto the 8 XCDs so that all items of one
-//     (batch, head) run on one XCD and share its L2.
+//     (batch, head) run on one XCD and share its L2;
+//   * bf16 path with a mask: an item whose key list holds a key of mask 1
+//     drops the listed blocks whose keys all have mask 0 (their
+//     probabilities are exactly zero), after one probe of the mask per
+//     listed block in its prologue.
 // The work decomposition itself (launch sizing, item mapping, key-block
 // lists) is in bbsa_schedule.h.
 #include <hip/hip_runtime.h>
@@ -436,12 +440,70 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
   // first two K tiles lie in the first block and do not need them.
   int rnd, rslot;
   KeyWalk walk = make_walk_base(p, it, lane, rnd, rslot);
-  const int n = __builtin_amdgcn_readfirstlane(walk.n_steps);   // >= 2, or 0 for an empty chunk
+  int n = __builtin_amdgcn_readfirstlane(walk.n_steps);   // >= 2, or 0 for an empty chunk
   // First key of step i: block i / steps_per_block of the list (a lane of
   // walk.blk), then 32 keys per step inside it.  Branch-free; uniform.
   const int lg_spb = walk.steps_per_block >> 1;      // steps_per_block is 2 or 4
   auto key_of = [&](int i) -> int {
     return __builtin_amdgcn_readlane(walk.blk, i >> lg_spb) * p.block + (i & (walk.steps_per_block - 1)) * kStep;
+  };
+
+  // Key blocks whose keys all have mask 0 hold scores 10000 below those of a
+  // key with mask 1.  Once the tile's list holds such a key, their
+  // probabilities are exactly zero in fp32 (and in exact arithmetic to far
+  // below fp64's range: e^-9890 and less), and they leave the reference max
+  // alone, so the tile drops them from its list and the result is the same.
+  // List position 0 stays (its transfers are issued before the list is
+  // final).  With query x key masking a query row of mask 0 sees no key
+  // bias at all, so only tiles whose rows all have mask 1 drop blocks.
+  // The probe reads two mask values per lane and 64 keys of each listed
+  // block (block 64: lanes 32-63 repeat lanes 0-31) after the prologue's
+  // wait, when the plan entries are in the list.
+  const bool wide = p.block > 64;
+  const int nblk0 = n >> lg_spb;
+  struct MaskProbe {
+    float m[8][2];
+  };
+  const int probe_voff = (wide ? 2 * lane : 2 * (lane & 31)) * 4;
+  const __amdgpu_buffer_rsrc_t mrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)mrow, (short)0, MASKING ? p.L * 4 : 0, kBufferWord3);
+  // Mask values of list positions [t0, t1) (at most 8; the rest repeat t1 - 1).
+  auto probe_load = [&](int t0, int t1, MaskProbe &pr) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int blk = __builtin_amdgcn_readlane(walk.blk, min(t0 + u, t1 - 1));
+      const auto mv = __builtin_amdgcn_raw_buffer_load_b64(mrs, probe_voff, blk * p.block * 4, 0);
+      pr.m[u][0] = __uint_as_float(mv[0]);
+      pr.m[u][1] = __uint_as_float(mv[1]);
+    }
+  };
+  // Bit t of padded: every key of position t has mask 0; valid: some key of
+  // the probed positions has mask 1.
+  auto probe_bits = [&](int t0, int t1, const MaskProbe &pr, uint64_t &padded, bool &valid) {
+    bool one = false;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t bit = (t0 + u < t1) ? (1ull << (t0 + u)) : 0ull;
+      if (!__builtin_amdgcn_ballot_w64(pr.m[u][0] != 0.0f || pr.m[u][1] != 0.0f)) padded |= bit;
+      one |= pr.m[u][0] == 1.0f || pr.m[u][1] == 1.0f;
+    }
+    valid |= __builtin_amdgcn_ballot_w64(one) != 0;
+  };
+  // Drop the padded positions (stable compaction: kept position t moves to
+  // the number of kept positions below it, dropped ones follow in order, a
+  // permutation of the 64 lanes that leaves lanes past the list in place).
+  // Returns the new step count.
+  auto drop_padded = [&](int n_in, uint64_t padded, bool valid) -> int {
+    if (!valid || (QK && __builtin_amdgcn_ballot_w64(mq[0] != 1.0f || mq[1] != 1.0f))) return n_in;
+    const int nblk = n_in >> lg_spb;
+    const uint64_t all = nblk >= 64 ? ~0ull : (1ull << nblk) - 1;
+    const uint64_t keep = (all & ~padded) | 1ull;
+    if (keep == all) return n_in;
+    const int nkeep = __builtin_popcountll(keep);
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u));
+    const int dst = ((keep >> lane) & 1) ? rank : nkeep + (lane - rank);
+    walk.blk = __builtin_amdgcn_ds_permute(dst * 4, walk.blk);
+    return nkeep * walk.steps_per_block;
   };
 
   // K and V of this (batch, head) as buffer resources (L x d rows): the DMA
@@ -596,6 +658,25 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
     dma_k(key_1, 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     merge_plan(p, walk, rnd, rslot);
+    constexpr bool kProbe = MASKING && !RAGGED;
+    const bool probe = kProbe && p.skip_padded;
+    MaskProbe pr_a, pr_b;
+    if (kProbe && probe) {
+      probe_load(0, min(nblk0, 8), pr_a);
+      if (nblk0 > 8) probe_load(8, min(nblk0, 16), pr_b);
+    }
+    if (kProbe && probe) {
+      uint64_t padded = 0;
+      bool valid = false;
+      probe_bits(0, min(nblk0, 8), pr_a, padded, valid);
+      if (nblk0 > 8) probe_bits(8, min(nblk0, 16), pr_b, padded, valid);
+      // Lists longer than 16 blocks (more than 11 random blocks): the rest, 8 at a time.
+      for (int t0 = 16; t0 < nblk0; t0 += 8) {
+        probe_load(t0, min(nblk0, t0 + 8), pr_a);
+        probe_bits(t0, min(nblk0, t0 + 8), pr_a, padded, valid);
+      }
+      n = __builtin_amdgcn_readfirstlane(drop_padded(n, padded, valid));
+    }
     f32x16 sc[2];
     {
       bf16x8 kc[4];

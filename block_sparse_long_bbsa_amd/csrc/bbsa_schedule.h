@@ -94,6 +94,7 @@ struct Params {
   int items_per_bh;          // n_global_items + middle items
   int bh_total;              // B * H
   int xcd_remap;             // 1: map workgroups so one (batch, head) stays on one XCD
+  int skip_padded;           // 1: bf16 tiles leave out key blocks whose keys are all padded
   int n_glob;                // full-row items before the first middle item (per XCD lane)
   FastDiv div_global;        // n_global_items
   FastDiv div_mid;           // middle items per (batch, head), at least 1
@@ -221,7 +222,8 @@ inline int setup_forward_ex(const void *q, const void *k, const void *v, const f
                             const int32_t *rand_attn, int B, int H, int L, int d, int block, int r,
                             void *out, float *lse, int dtype, unsigned flags, Launch *launch) {
   if (!q || !k || !v || !out || !launch) return BBSA_ERR_ARG;
-  if (flags & ~(unsigned)(BBSA_FLAG_PAD_TO_BLOCK | BBSA_FLAG_QUERY_KEY_MASK)) return BBSA_ERR_ARG;
+  if (flags & ~(unsigned)(BBSA_FLAG_PAD_TO_BLOCK | BBSA_FLAG_QUERY_KEY_MASK | BBSA_FLAG_KEEP_PADDED_BLOCKS))
+    return BBSA_ERR_ARG;
   // The kernels move q, k, v, out and the mask in 16-byte pieces.
   auto misaligned = [](const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
@@ -254,6 +256,7 @@ inline int setup_forward_ex(const void *q, const void *k, const void *v, const f
   p.B = B; p.H = H; p.L = L; p.nb = nb; p.block = block; p.r = r;
   p.mode = (mask ? kModeMask : 0) | (ragged ? kModeRagged : 0) |
            ((mask && (flags & BBSA_FLAG_QUERY_KEY_MASK)) ? kModeQK : 0);
+  p.skip_padded = (mask && !ragged && dtype == BBSA_BF16 && !(flags & BBSA_FLAG_KEEP_PADDED_BLOCKS)) ? 1 : 0;
   p.qtiles = block / kQT;
   p.n_rows_global = full ? nb : 2;
   // Full rows are cut into chunks of about 1024 keys (bf16) or 256 keys (the

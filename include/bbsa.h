@@ -39,7 +39,8 @@ typedef enum { BBSA_BF16 = 0, BBSA_F32 = 1 } bbsa_dtype;
 /* Options of bbsa_forward_ex (bit flags). */
 enum {
   BBSA_FLAG_PAD_TO_BLOCK = 1,   /* L need not be a multiple of the block */
-  BBSA_FLAG_QUERY_KEY_MASK = 2  /* bias -10000 (1 - mask[query] mask[key]) */
+  BBSA_FLAG_QUERY_KEY_MASK = 2, /* bias -10000 (1 - mask[query] mask[key]) */
+  BBSA_FLAG_KEEP_PADDED_BLOCKS = 4 /* also compute key blocks whose keys are all padded */
 };
 
 /* Status codes. */
@@ -145,7 +146,15 @@ int bbsa_truncate_rand_attn(const int32_t *src, int H, int nb_src, int r, int32_
  *            and mask; rand_attn 4-byte aligned), else BBSA_ERR_ARG.
  * mask:      device float32 [B, L], 1 = valid key, 0 = padding (fractional
  *            values act through the bias -10000 * (1 - mask)); NULL = all
- *            keys valid.
+ *            keys valid.  On the bf16 path with a mask (L a multiple of the
+ *            block), a 64-row query tile whose key list holds a key of mask 1
+ *            leaves out the listed key blocks whose mask values are all 0
+ *            (except the first block of its list): their probabilities are
+ *            exactly zero in fp32, so the output and the log-sum-exp are
+ *            those of computing them, as long as no padded key's score
+ *            exceeds a valid key's score of the same tile by about 9890 (the
+ *            -10000 bias would not mask it either).  bbsa_forward_ex's
+ *            BBSA_FLAG_KEEP_PADDED_BLOCKS computes every block.
  * rand_attn: device int32 [H, nb-2, r] from bbsa_plan_rand_attn; ignored
  *            (may be NULL) when the call falls back to full attention.  A
  *            plan that breaks the invariants never causes an out-of-bounds
@@ -204,7 +213,10 @@ int bbsa_forward(const void *q, const void *k, const void *v, const float *mask,
  *     mask from (BigBirdMasks' einsum), instead of the key-side
  *     -10000 * (1 - mask[b, u]).  Rows of valid queries are unchanged; a
  *     padded query row gets the same bias on every key, i.e. a softmax of
- *     its raw scores.  No effect without a mask.
+ *     its raw scores.  No effect without a mask.  (Padded key blocks are
+ *     then left out only by tiles whose query rows all have mask 1.)
+ *   BBSA_FLAG_KEEP_PADDED_BLOCKS: compute every key block of the pattern,
+ *     also those whose keys all have mask 0 (see `mask` under bbsa_forward).
  * lse: device float32 [B, H, L], 4-byte aligned, caller-owned, or NULL: the
  *     natural log-sum-exp of each query row's scores (bias included) over
  *     the keys it attends, the quantity a recompute-based backward needs.

@@ -93,7 +93,8 @@ def test_forward_ex_validates(lib):
     # usual argument errors; no HIP call happens for any of them.
     def ex(L=1024, flags=0, lse=None, q=FAKE):
         return lib.bbsa_forward_ex(q, FAKE, FAKE, None, FAKE, 1, 1, L, 64, 64, 3, FAKE, lse, None, 0, flags)
-    assert ex(flags=4) == bbsa.BBSA_ERR_ARG
+    assert ex(flags=8) == bbsa.BBSA_ERR_ARG
+    assert ex(flags=0x80000000) == bbsa.BBSA_ERR_ARG
     assert ex(L=1000) == bbsa.BBSA_ERR_SHAPE
     assert ex(q=None) == bbsa.BBSA_ERR_ARG
     assert ex(L=1000, flags=1, lse=ctypes.c_void_p(0x1002)) == bbsa.BBSA_ERR_ARG   # lse 4-byte aligned
