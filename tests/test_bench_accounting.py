@@ -47,3 +47,50 @@ def test_multi_gpu_request_is_refused():
     res = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def _executed_by_rows(w, mask, plan, chunks):
+    """The executed share restated row by row from the pattern itself: a
+    middle row lists block 0 first, a global row's key chunk c covers blocks
+    [c nb / chunks, (c + 1) nb / chunks) and lists its first block first; a
+    list with a key of mask 1 drops its fully padded blocks except the first.
+    (For these workloads each 64-row tile of a query block has the same list.)"""
+    nb, blk = w.nb, w.block
+    blocks = mask.reshape(w.B, nb, blk)
+    padded = (blocks == 0).all(axis=2)
+    one = (blocks == 1).any(axis=2)
+    total = executed = 0
+
+    def add(b, lst):
+        nonlocal total, executed
+        total += len(lst)
+        drop = sum(padded[b, x] for x in lst[1:]) if any(one[b, x] for x in lst) else 0
+        executed += len(lst) - drop
+
+    for b in range(w.B):
+        for h in range(w.H):
+            M = oracle.block_mask(nb, plan[h])
+            for i in range(nb):
+                if i in (0, nb - 1):
+                    for c in range(chunks):
+                        add(b, list(range(c * nb // chunks, (c + 1) * nb // chunks)))
+                else:
+                    keys = [int(x) for x in np.nonzero(M[i])[0]]
+                    add(b, [0] + [x for x in keys if x != 0])
+    return executed / total
+
+
+@pytest.mark.parametrize("wid,chunks", [(2, 4), (3, 4), (4, 16), (5, 32)])
+def test_executed_pair_fraction(wid, chunks):
+    """bench.executed_pair_fraction (the library's work map plus the mask)
+    against the same rule applied to the pattern's block mask."""
+    from block_sparse_long_bbsa_amd import bbsa
+    w = workloads.WORKLOADS[wid]
+    x = workloads.make_inputs(wid)
+    plan = bbsa.bbsa_plan_rand_attn(w.H, w.nb, w.r, w.plan_seed)
+    got = bench.executed_pair_fraction(w, x["mask"], plan, bbsa)
+    assert got == pytest.approx(_executed_by_rows(w, x["mask"], plan, chunks), rel=1e-12)
+    if wid == 4:
+        assert got == 1.0     # no padding: nothing is left out
+    else:
+        assert 0.6 < got < 0.9
