@@ -166,7 +166,7 @@ def executed_pair_fraction(w, mask, plan, bbsa) -> float:
     from the library's work map) holds a key of mask 1, except the block at
     list position 0.  The useful flops above count every pattern pair,
     padding included; this is for reporting the work actually done."""
-    if w.dtype != "bf16":
+    if w.dtype != "bf16" or mask is None:
         return 1.0
     st, _, rec = bbsa.bbsa_work_map(w.B, w.H, w.L, w.d, w.block, w.r, bbsa.BBSA_BF16, plan)
     if st < 0 or len(rec) == 0:
@@ -215,7 +215,7 @@ class Runner:
             q, k, v = (t.clone() for t in base)
             self.sets.append((q, k, v, torch.empty_like(q)))
         del base
-        self.mask = torch.from_numpy(self.inp["mask"]).to(dev)
+        self.mask = torch.from_numpy(self.inp["mask"]).to(dev) if w.masked else None
         self.ra = torch.from_numpy(self.plan).to(dev)
         self.stream = torch.cuda.current_stream(dev)
         self.bbsa = bbsa
@@ -373,7 +373,7 @@ def main():
     roof, flops, nbytes = roofline(w, ms)
     roof["traffic"] = read_traffic(w.name)
     roof["kernel"] = "bbsa_attn_bf16" if w.dtype == "bf16" else "bbsa_attn_f32"
-    add_executed(roof, executed_pair_fraction(w, run.inp["mask"], run.plan, bbsa))
+    add_executed(roof, executed_pair_fraction(w, run.inp["mask"] if w.masked else None, run.plan, bbsa))
     # The step is one attention-kernel launch (plus the merge kernel only for
     # rows longer than 4096 keys), so the average launch duration over the
     # timed region is the step time; per-launch events (which add their own
@@ -404,7 +404,7 @@ def main():
         r2.preroll(args.preroll)
         ms2 = r2.timed(args.steps, args.warmup)
         rf2, fl2, nb2 = roofline(r2.w, ms2)
-        add_executed(rf2, executed_pair_fraction(r2.w, r2.inp["mask"], r2.plan, bbsa))
+        add_executed(rf2, executed_pair_fraction(r2.w, r2.inp["mask"] if r2.w.masked else None, r2.plan, bbsa))
         v2 = fl2 / (ms2 * 1e-3) / 1e12
         log(f"{r2.w.name}: step {ms2 * 1e3:.2f} us; {v2:.1f} useful TFLOP/s; frac {rf2['frac']} "
             f"({rf2['bound']}); MFMA {rf2['mfma_frac']} HBM {rf2['hbm_frac']}")

@@ -41,6 +41,7 @@ class Workload:
     plan_seed: int
     description: str = ""
     extra_plan_seeds: tuple = field(default_factory=tuple)
+    masked: bool = True         # the call gets the padding mask (False: no mask, every key valid)
 
     @property
     def nb(self) -> int:
@@ -56,7 +57,7 @@ WORKLOADS = {
                 "Pegasus-large encoder shape; valid length U{1024..4096} (partial blocks)",
                 extra_plan_seeds=(1,)),
     4: Workload(4, "bf16_B2_H12_L16384_b64_r3", 2, 12, 16384, 64, 64, 3, "bf16", 0,
-                "long context, no padding"),
+                "long context, no padding (the call gets no mask)", masked=False),
     5: Workload(5, "bf16_B1_H16_L32768_b128_r2", 1, 16, 32768, 64, 128, 2, "bf16", 0,
                 "block 128; 1% of keys per (b,h) get +4 on every element; last 10% padded"),
 }

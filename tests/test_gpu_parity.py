@@ -211,7 +211,7 @@ def test_workload_parity(wid, seed):
     announce(f"workload {wid} {w.name} plan seed {plan_seed}")
     inp = workloads.make_inputs(wid)
     cplan, oplan = plans(w.H, w.nb, w.r, plan_seed)
-    got, st = run_gpu(inp, w.block, w.r, w.dtype, cplan)
+    got, st = run_gpu(inp, w.block, w.r, w.dtype, cplan, use_mask=w.masked)
     assert st == bbsa.BBSA_OK
     # Every output row was written (the buffer started as NaN).
     assert np.isfinite(got).all(), "non-finite output: some row was not written"
