@@ -288,10 +288,13 @@ def bbsa_attention_probs(q, k, mask, rand_attn, block: int, r: int, probs=None, 
 
 
 def bbsa_backward(q, k, v, out, dout, lse, mask, rand_attn, block: int, r: int, dq=None, dk=None, dv=None,
-                  delta=None, stream=None, pad_to_block: bool = False, query_key_mask: bool = False):
+                  delta=None, stream=None, pad_to_block: bool = False, query_key_mask: bool = False,
+                  keep_padded_blocks: bool = False):
     """Gradients (dq, dk, dv) of the forward's output; ``out`` and ``lse``
     come from ``bbsa_forward_ex`` with the same arguments (see
-    include/bbsa.h).  Returns ``(dq, dk, dv, status)``."""
+    include/bbsa.h).  keep_padded_blocks: also compute the steps whose keys
+    all have mask 0 (left out by default where they add nothing).
+    Returns ``(dq, dk, dv, status)``."""
     import torch
     B, H, L, d = q.shape
     for t in (out, dout):
@@ -308,7 +311,8 @@ def bbsa_backward(q, k, v, out, dout, lse, mask, rand_attn, block: int, r: int, 
     if delta is None:
         delta = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     args = _marshal(q, k, v, mask, rand_attn, block, r, out, stream, pad=pad_to_block)
-    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0)
+    flags = (BBSA_FLAG_PAD_TO_BLOCK if pad_to_block else 0) | (BBSA_FLAG_QUERY_KEY_MASK if query_key_mask else 0) | \
+        (BBSA_FLAG_KEEP_PADDED_BLOCKS if keep_padded_blocks else 0)
     cargs = [args[0], args[1], args[2], out.data_ptr(), dout.data_ptr(), lse.data_ptr(), args[3], args[4]] + \
         list(args[5:11]) + [dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), args[12], args[13], flags]
     with torch.cuda.device(q.device):

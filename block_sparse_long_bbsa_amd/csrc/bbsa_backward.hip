@@ -84,6 +84,7 @@ struct BwdParams {
   const int32_t *rand_attn;  // [H, nb-2, r] or null (fallback)
   float *delta;              // [B, H, L]: D = rowsum(dO * out), written by the dq kernel
   float *rterm;              // [B, H, L]: -(log2e lse - (1 - mq) log2e kPadBias), written by the dq kernel
+  int *live;                 // [B, H, nb * tiles]: 1 if some row of the query tile may weigh a padded key (dq kernel)
   bf16_t *dq, *dk, *dv;
   float *ws;                 // split partials of the global rows (dq) and columns (dk, dv)
   int B, H, L, nb, block, r;
@@ -97,7 +98,16 @@ struct BwdParams {
   int mid_items;             // per pair: (nb - 2) * tiles (0 on the fallback)
   int n_glob_lane;           // global items before the first middle item, per XCD lane
   int64_t n_part;            // partials per gradient
+  int skip;                  // 1: steps whose keys are all padded are skipped for rows that attend a real key
 };
+
+// A query row whose log-sum-exp exceeds -5000 (natural units) attends keys
+// far above the padding bias: a key of mask 0 then has a probability
+// exp(s - 10000 - lse) below exp(s - 5000), exactly zero in fp32 for any
+// score s below about 4900, so a step whose keys all have mask 0 adds
+// exactly nothing to such rows' dQ, or to its keys' dK and dV (the forward
+// leaves the same blocks out).  In log2 units: lse2 > -kLiveLog2.
+constexpr float kLiveLog2 = 5000.0f * 1.4426950408889634f;
 
 // Work item: a 32-row tile of block blk (a query block for dq, a key block
 // for dk/dv) of pair bh; a global row or column is split into `chunks`
@@ -389,9 +399,9 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   } else {
     pos1 = 2 + ((i == 1 || i == p.nb - 2) ? 2 : 3) + p.r;
   }
-  const int n_steps = __builtin_amdgcn_readfirstlane((pos1 - pos0) * spb);
+  int n_steps = __builtin_amdgcn_readfirstlane((pos1 - pos0) * spb);
   // The middle row's key blocks, lane t holding list position t (at most 64).
-  const int blocks = it.glob ? 0 : list_block(p, plan_row, i, min(lane, pos1 - 1));
+  int blocks = it.glob ? 0 : list_block(p, plan_row, i, min(lane, pos1 - 1));
   auto key_of = [&](int st) {
     const int pos = pos0 + (st >> lg_spb);
     const int row =
@@ -444,6 +454,13 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   // The exponent of P in log2 units is s log2e + (1 - m) cpad - lse2 for a
   // key of mask value m: the bias term is exactly 0 for m = 1.
   const float cpad = mq * kPadBias * kLog2e;
+  // Steps whose 32 keys all have mask 0 add nothing when every row of the
+  // tile attends a real key (and, under query x key masking, has mask 1;
+  // rows past L have zero Q and dO).
+  const bool tile_live = __builtin_amdgcn_ballot_w64(qlive && ((p.qk && mq != 1.0f) || lse2 <= -kLiveLog2)) != 0;
+  const bool drop_dead = MASKED && p.skip && !tile_live;
+  if (MASKED && p.skip && lane == 0 && (!it.glob || it.chunk == 0))
+    p.live[((int64_t)bh * p.nb + i) * p.tiles + it.tile] = tile_live ? 1 : 0;
 
   auto issue = [&](auto S, int st) {
     const int key0 = key_of(st);
@@ -453,10 +470,52 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   };
   constexpr int kPerStep = MASKED ? 9 : 8;
 
+  // A middle row whose rows all attend a real key leaves out the listed
+  // blocks whose keys all have mask 0 (list position 0, in flight first,
+  // stays): one 8-byte mask probe per lane and listed block, issued before
+  // the first step's transfers, then a stable compaction of the list.
+  const bool compact = MASKED && drop_dead && !it.glob && p.L % p.block == 0;
+  const int npos = pos1 - pos0;
+  float pm[8][2];
+  auto probe_load = [&](int t0) {
+    const int off = (p.block > 64 ? 2 * lane : 2 * (lane & 31)) * 4;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int blk = __builtin_amdgcn_readlane(blocks, min(t0 + u, npos - 1));
+      const auto mv = __builtin_amdgcn_raw_buffer_load_b64(mrs, off, blk * p.block * 4, 0);
+      pm[u][0] = __uint_as_float(mv[0]);
+      pm[u][1] = __uint_as_float(mv[1]);
+    }
+  };
+  uint64_t padded = 0;
+  auto probe_bits = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (t0 + u < npos && !__builtin_amdgcn_ballot_w64(pm[u][0] != 0.0f || pm[u][1] != 0.0f))
+        padded |= 1ull << (t0 + u);
+  };
+  if (compact) probe_load(0);
+
   // Transfers go out for every step below n_steps + 2, so the compiler's
   // own wait before each slot's reads also counts only that slot's.
   f32x16 dq[2] = {zero16(), zero16()};
   issue(SlotId<0>{}, 0);
+  if (compact) {
+    probe_bits(0);
+    for (int t0 = 8; t0 < npos; t0 += 8) {
+      probe_load(t0);
+      probe_bits(t0);
+    }
+    const uint64_t all = npos >= 64 ? ~0ull : (1ull << npos) - 1;
+    const uint64_t keep = (all & ~padded) | 1ull;
+    if (keep != all) {
+      const int nkeep = __builtin_popcountll(keep);
+      const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u));
+      const int dst = ((keep >> lane) & 1) ? rank : nkeep + (lane - rank);
+      blocks = __builtin_amdgcn_ds_permute(dst * 4, blocks);
+      n_steps = __builtin_amdgcn_readfirstlane(nkeep * spb);
+    }
+  }
   if constexpr (kSlots == 3) issue(SlotId<1>{}, 1);
   run_steps(n_steps, [&](auto S, int st) {
     wait_step<(kSlots - 2) * kPerStep>();
@@ -470,11 +529,17 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
     // (the last block of a ragged length) carry the bias.
     // A step whose 32 keys are all real and unmasked (the common case)
     // takes x = -lse2 throughout.
-    bool plain;
-    if (MASKED) plain = __builtin_amdgcn_ballot_w64(*(const float *)(mk(S) + 4 * c) != 1.0f) == 0;
-    else plain = key0 + kT <= p.L;
+    bool plain, dead = false;
+    if (MASKED) {
+      const float mkey = *(const float *)(mk(S) + 4 * c);
+      plain = __builtin_amdgcn_ballot_w64(mkey != 1.0f) == 0;
+      if (drop_dead) dead = __builtin_amdgcn_ballot_w64(mkey != 0.0f) == 0;
+    } else {
+      plain = key0 + kT <= p.L;
+    }
     // The transfers of step st + kSlots - 1 go into the slot step st - 1 read.
     issue(IssueSlot<decltype(S)::value>{}, st + kSlots - 1);
+    if (dead) return;
     f32x16 sc = mfma(kr[0], qf[0], zero16());   // S^T[key][query c]
     f32x16 dp = mfma(vr[0], df[0], dinit);      // D - dP^T[key][query c]
 #pragma unroll
@@ -578,6 +643,10 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
   // keys all have kb2 = 0 takes x = 0.
   const float kb2 = kPadBias * (1.0f - mask_at(p, mrow, k0 + c)) * kLog2e;
   const bool plain = __builtin_amdgcn_ballot_w64(kb2 != 0.0f) == 0;
+  // A tile whose keys all have mask 0 (or lie past L) gets nothing from the
+  // query rows that attend a real key (and have mask 1 under query x key
+  // masking): such steps are skipped.
+  const bool dead_keys = p.skip && __builtin_amdgcn_ballot_w64(mask_at(p, mrow, k0 + c) != 0.0f) == 0;
   // The dP product runs on -V from an accumulator holding D (the step's D
   // values, read from LDS): it yields D - dP, and dS = -P (D - dP).
   negate(vf);
@@ -587,10 +656,31 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
   // Walk the query blocks of list positions [0, n) (block of position t:
   // from the LDS list, or first + t for a range), 32 queries a step.
   auto walk = [&](int n, bool from_list, int first) {
+    // A tile whose keys all have mask 0 walks only the query blocks with a
+    // tile whose rows may weigh a padded key (the dq kernel's flags): the
+    // others add exactly nothing.  Lane t holds list position t (lists of
+    // up to 64 blocks; longer ones are walked whole).
+    bool compacted = false;
+    int plist = 0;
+    if (dead_keys && n <= 64) {
+      const int blk = from_list ? blist[min(lane, 127)] : first + lane;
+      const int blk_c = min(max(blk, 0), p.nb - 1);   // lanes past the list read a valid flag, unused
+      bool live = false;
+      for (int s2 = 0; s2 < p.tiles; ++s2) live |= p.live[((int64_t)bh * p.nb + blk_c) * p.tiles + s2] != 0;
+      live = live && lane < n;
+      const uint64_t keep = __builtin_amdgcn_ballot_w64(live);
+      const int nkeep = __builtin_popcountll(keep);
+      const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0u));
+      const int dst = ((keep >> lane) & 1) ? rank : nkeep + (lane - rank);
+      plist = __builtin_amdgcn_ds_permute(dst * 4, blk);
+      n = nkeep;
+      compacted = true;
+    }
     const int n_steps = __builtin_amdgcn_readfirstlane(n * spb);
     auto row_of = [&](int st) {
       const int t = min(st >> lg_spb, 127);
-      const int row = (from_list ? blist[t] : first + t) * p.block + (st & (spb - 1)) * kT;
+      const int blk = compacted ? __builtin_amdgcn_readlane(plist, min(t, 63)) : (from_list ? blist[t] : first + t);
+      const int row = blk * p.block + (st & (spb - 1)) * kT;
       return __builtin_amdgcn_readfirstlane(st < n_steps ? row : kNoRow);
     };
     auto issue = [&](auto S, int st) {
@@ -624,6 +714,14 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
         else mqv[jj] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
       }
       issue(IssueSlot<decltype(S)::value>{}, st + kSlots - 1);
+      if (dead_keys) {
+        bool live = false;   // some row whose padded keys may carry weight
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) live |= rt[jj][ii] >= kLiveLog2 || (QK && mqv[jj][ii] != 1.0f);
+        if (!__builtin_amdgcn_ballot_w64(live)) return;
+      }
       f32x16 dinit;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
@@ -775,6 +873,7 @@ extern "C" int bbsa_backward(const void *q, const void *k, const void *v, const 
   p.B = B; p.H = H; p.L = L; p.nb = ln.p.nb; p.block = block; p.r = r;
   p.full = ln.full ? 1 : 0;
   p.qk = (ln.p.mode & kModeQK) ? 1 : 0;
+  p.skip = (mask && !(flags & BBSA_FLAG_KEEP_PADDED_BLOCKS)) ? 1 : 0;
   p.tiles = block / kT;
   p.chunks = std::max(std::min(p.nb, 2), (p.nb + kChunkBlocks - 1) / kChunkBlocks);
   p.n_grows = ln.full ? p.nb : 2;
@@ -791,15 +890,18 @@ extern "C" int bbsa_backward(const void *q, const void *k, const void *v, const 
       (int64_t)p.glob_items * pairs_per_lane > 0x7fffffff)
     return BBSA_ERR_UNSUPPORTED;
   p.n_glob_lane = (int)n_glob_lane;
-  // Workspace: the row terms, then (with split rows) the partials.
+  // Workspace: the row terms, the query tiles' flags, then (with split rows)
+  // the partials.
   {
     const size_t rt_floats = ((size_t)rows + 63) / 64 * 64;
+    const size_t live_ints = ((size_t)bh * p.nb * p.tiles + 63) / 64 * 64;
     const size_t part_floats = p.chunks > 1 ? (size_t)(3 * p.n_part) * kT * kD : 0;
     float *ws = nullptr;
-    const int rc = library_workspace((rt_floats + part_floats) * sizeof(float), stream, &ws);
+    const int rc = library_workspace((rt_floats + live_ints + part_floats) * sizeof(float), stream, &ws);
     if (rc != BBSA_OK) return rc;
     p.rterm = ws;
-    p.ws = ws + rt_floats;
+    p.live = (int *)(ws + rt_floats);
+    p.ws = ws + rt_floats + live_ints;
   }
   if (mask) hipLaunchKernelGGL(bbsa_bwd_dq<true>, dim3((unsigned)grid), dim3(64), 0, stream, p);
   else hipLaunchKernelGGL(bbsa_bwd_dq<false>, dim3((unsigned)grid), dim3(64), 0, stream, p);

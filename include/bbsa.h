@@ -280,10 +280,16 @@ int bbsa_attention_probs(const void *q, const void *k, const float *mask, const 
  *
  * BBSA_BF16: MFMA kernels; three kernels on `stream` (two when nb = 1),
  * using the library's workspace for `stream` (B * H * L floats of row
- * terms, plus fp32 partials of the split global rows and columns:
+ * terms, B * H * nb * block / 32 ints of query-tile flags, plus fp32
+ * partials of the split global rows and columns:
  * 3 * B * H * 2 * block * 64 * c floats with nb = ceil(L / block) and
  * c = max(min(nb, 2), ceil(nb / 64)) chunks per row, or nb in place of 2 on
  * the full-attention fallback).
+ * With a mask (bf16), steps whose keys all have mask 0 are left out for the
+ * query rows whose lse exceeds -5000 (and whose mask is 1 under query x key
+ * masking): their probabilities are exactly zero in fp32 for scores below
+ * about 4900, so the gradients equal those of computing them;
+ * BBSA_FLAG_KEEP_PADDED_BLOCKS computes every step.
  * BBSA_F32: an fp32 path on the vector units (three kernels; workspace
  * 2 * B * H * L floats), which recomputes each row's normaliser relative to
  * its padding-bias level as the fp32 forward does, so rows whose keys all

@@ -150,3 +150,84 @@ def test_full_size_skip_equals_keep(wid):
     assert torch.isfinite(out.float()).all()
     assert torch.equal(out, out_k)
     assert torch.equal(lse, lse_k)
+
+
+# Backward: a step whose 32 keys all have mask 0 adds exactly nothing to the
+# rows whose log-sum-exp shows a real key (and whose own mask is 1 under
+# query x key masking), so the kernels skip it; computing every step
+# (BBSA_FLAG_KEEP_PADDED_BLOCKS) gives the same gradients bit for bit.
+
+def _backward(q, k, v, dout, mask, plan, block, r, qk=False, pad=False):
+    """One forward (saving the LSE), then the backward twice on its output:
+    skipping the padded steps and computing every step."""
+    out, lse, st = bbsa.bbsa_forward_ex(q, k, v, mask, plan, block, r, return_lse=True, query_key_mask=qk,
+                                        pad_to_block=pad, warn_fallback=False)
+    res = []
+    for keep in (False, True):
+        grads = [torch.full_like(q, float("nan")) for _ in range(3)]
+        dq, dk, dv, st2 = bbsa.bbsa_backward(q, k, v, out, dout, lse, mask, plan, block, r, dq=grads[0],
+                                             dk=grads[1], dv=grads[2], query_key_mask=qk, pad_to_block=pad,
+                                             keep_padded_blocks=keep)
+        torch.cuda.synchronize()
+        assert st >= 0 and st2 == st
+        res.append((dq, dk, dv))
+    return res
+
+
+BWD_CASES = [
+    # (B, H, L, block, r, seed, fraction of padded blocks, query x key masking, leading padding)
+    (2, 2, 2048, 64, 3, 31, 0.3, False, False),
+    (2, 2, 2048, 64, 3, 32, 0.3, True, False),
+    (1, 2, 4096, 128, 2, 33, 0.25, False, True),
+    (2, 2, 704, 64, 3, 34, 0.4, False, False),      # full-attention fallback
+]
+
+
+@pytest.mark.parametrize("B,H,L,block,r,seed,frac,qk,lead", BWD_CASES)
+def test_backward_padded_steps(B, H, L, block, r, seed, frac, qk, lead):
+    announce(f"backward padded steps B{B} H{H} L{L} b{block} r{r} qk{qk} lead{lead}")
+    rng = np.random.default_rng(seed)
+    inp = workloads.make_case(B, H, L, 64, seed, "bf16")
+    nb = L // block
+    full = L <= (5 + 2 * r) * block
+    c_plan, o_plan = plans(H, nb, r, seed) if not full else (None, np.zeros((H, nb - 2, r), np.int32))
+    m = np.ones((B, L), np.float32)
+    for b in range(B):
+        for kb in rng.choice(np.arange(nb), size=max(1, int(frac * nb)), replace=False):
+            m[b, kb * block:(kb + 1) * block] = 0.0
+    if lead:
+        m[:, :block] = 0.0
+    inp["mask"] = m
+    dout_np = workloads.round_to_bf16(rng.standard_normal((B, H, L, 64)).astype(np.float32))
+    q, k, v, dout = (to_dev(x, torch.bfloat16) for x in (inp["q"], inp["k"], inp["v"], dout_np))
+    mask = to_dev(m, torch.float32)
+    ra = None if c_plan is None else torch.from_numpy(c_plan).cuda()
+    got, ref = _backward(q, k, v, dout, mask, ra, block, r, qk=qk)
+    for name, g, w in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.isfinite(g.float()).all(), f"{name}: unwritten entries"
+        assert torch.equal(g, w), f"{name}: skipping padded steps changed the gradient"
+    want = oracle.backward(inp["q"], inp["k"], inp["v"], m, o_plan, block, dout_np, query_key_mask=qk)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        g = g.float().cpu().numpy().astype(np.float64)
+        s = max(1.0, float(np.abs(w).max()))
+        err = np.abs(g - w)
+        announce(f"backward padded steps {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} scale={s:.3g}")
+        assert err.max() <= 2e-2 * s and err.mean() <= 2e-3 * s, f"{name}: max abs {err.max()}"
+
+
+def test_backward_full_size_skip_equals_keep():
+    """The BigBird-base workload's gradients with and without the skipped
+    steps, bit for bit."""
+    w = workloads.WORKLOADS[2]
+    announce(f"backward skip vs keep at full size {w.name}")
+    x = workloads.make_inputs(2)
+    rng = np.random.Generator(np.random.PCG64(401))
+    dout = to_dev(workloads.round_to_bf16(rng.standard_normal(x["q"].shape).astype(np.float32)), torch.bfloat16)
+    q, k, v = (to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    mask = to_dev(x["mask"], torch.float32)
+    c_plan, _ = plans(w.H, w.nb, w.r, w.plan_seed)
+    ra = torch.from_numpy(c_plan).cuda()
+    got, ref = _backward(q, k, v, dout, mask, ra, w.block, w.r)
+    for name, g, r_ in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.isfinite(g.float()).all(), f"{name}: unwritten entries"
+        assert torch.equal(g, r_), f"{name} differs"
