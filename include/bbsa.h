@@ -354,7 +354,9 @@ int bbsa_timing_read(double *main_ms, double *combine_ms, int *calls);
  * call).  For the shape, dtype and flags of a bbsa_forward_ex call (flags 0:
  * a bbsa_forward call) with host plan
  * `rand_attn` (may be NULL on the fallback), runs on the host the same item
- * mapping and key-list construction the kernels run, and writes one record
+ * mapping and key-list construction the kernels run (the lists as built,
+ * before a masked bf16 call leaves out its fully padded key blocks, which
+ * depends on the mask's values), and writes one record
  * of BBSA_WORK_RECORD_INTS int32 per work item (a 64-row query tile against
  * a key list) of the attention kernel:
  *   [0] workgroup  [1] wavefront  [2] 0 (reserved)
