@@ -231,3 +231,28 @@ def test_backward_full_size_skip_equals_keep():
     for name, g, r_ in zip(("dq", "dk", "dv"), got, ref):
         assert torch.isfinite(g.float()).all(), f"{name}: unwritten entries"
         assert torch.equal(g, r_), f"{name} differs"
+
+
+def test_keep_flag_covers_scores_beyond_the_padding_bias():
+    """Scores so large that a padded key still outweighs the valid ones
+    under the -10000 bias (here 16384 - 10000 against about 0): the
+    default call leaves such a key out (its documented limit), while
+    BBSA_FLAG_KEEP_PADDED_BLOCKS computes it and matches the oracle."""
+    B, H, L, block, r, seed = 1, 1, 1536, 64, 3, 41
+    announce("padded key beyond the bias, keep flag")
+    inp = workloads.make_case(B, H, L, 64, seed, "bf16")
+    nb = L // block
+    pad_blk = nb - 4
+    inp["q"][:] = 16.0                           # every query row: q = 16 (exact in bf16)
+    inp["k"] = workloads.round_to_bf16(inp["k"] * np.float32(0.01))   # other scores: about N(0, 1.6)
+    inp["k"][0, 0, pad_blk * block:(pad_blk + 1) * block, :] = 16.0   # padded keys: score 64 * 256 = 16384
+    m = np.ones((B, L), np.float32)
+    m[:, pad_blk * block:(pad_blk + 1) * block] = 0.0
+    inp["mask"] = m
+    c_plan, o_plan = plans(H, nb, r, seed)
+    q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    mask = to_dev(m, torch.float32)
+    ra = torch.from_numpy(c_plan).cuda()
+    out_k, _ = _run(q, k, v, mask, ra, block, r, keep=True)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], m, o_plan, block)
+    assert_close(out_k.float().cpu().numpy().astype(np.float64), want, "bf16", "keep flag, scores beyond the bias")
