@@ -180,6 +180,7 @@ BWD_CASES = [
     (2, 2, 2048, 64, 3, 32, 0.3, True, False),
     (1, 2, 4096, 128, 2, 33, 0.25, False, True),
     (2, 2, 704, 64, 3, 34, 0.4, False, False),      # full-attention fallback
+    (1, 2, 2048, 64, 12, 35, 0.3, False, False),    # 17-block lists: the probe's three passes
 ]
 
 
