@@ -138,6 +138,29 @@ def test_backward_bigbird_base_workload():
         check([g[sl] for g in got], want, f"backward {w.name} pair {bh}")
 
 
+def test_backward_pegasus_workload():
+    # The Pegasus-large encoder workload (B8 H16 L4096, valid lengths that
+    # end inside a block, so padded and half-padded blocks both occur)
+    # through the backward; every gradient row of two (batch, head) pairs on
+    # different XCD lanes and batches is compared.
+    w = workloads.WORKLOADS[3]
+    announce("backward Pegasus-large workload")
+    inp = workloads.make_inputs(3)
+    rng = np.random.Generator(np.random.PCG64(402))
+    dout = bf16_exact(rng.standard_normal(inp["q"].shape).astype(np.float32))
+    cplan, oplan = plans(w.H, w.nb, w.r, w.plan_seed)
+    got, st = run_backward(inp, dout, w.block, w.r, cplan)
+    assert st == bbsa.BBSA_OK
+    for g in got:
+        assert np.isfinite(g).all()
+    for bh in (5, 122):
+        b, h = divmod(bh, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        want = oracle.backward(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["mask"][b:b + 1], oplan[h:h + 1],
+                               w.block, dout[sl])
+        check([g[sl] for g in got], want, f"backward {w.name} pair {bh}")
+
+
 F32_CASES = [
     # B, H, L, block, r, valid, pad, qk, seed
     (1, 2, 1024, 64, 3, (1024,), False, False, 21),       # the fp32 workload's shape
