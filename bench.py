@@ -221,10 +221,16 @@ class Runner:
         self.bbsa = bbsa
         self.torch = torch
 
+    keep_padded = False   # --keep-padded-blocks: compute every pattern block (for comparison)
+
     def step(self, i):
         q, k, v, o = self.sets[i % self.n_sets]
-        self.bbsa.bbsa_forward(q, k, v, self.mask, self.ra, self.w.block, self.w.r, out=o,
-                               stream=self.stream)
+        if self.keep_padded:
+            self.bbsa.bbsa_forward_ex(q, k, v, self.mask, self.ra, self.w.block, self.w.r, out=o,
+                                      stream=self.stream, keep_padded_blocks=True)
+        else:
+            self.bbsa.bbsa_forward(q, k, v, self.mask, self.ra, self.w.block, self.w.r, out=o,
+                                   stream=self.stream)
 
     def preroll(self, seconds):
         """Untimed steps for a fixed wall time before the warm-up steps: the
@@ -284,21 +290,24 @@ class Runner:
 
 
 def backward_leg(run, args, torch, bbsa):
-    """Time one backward step (the row kernel, the dq kernel and the dk/dv
-    kernel) on the headline workload's inputs, after a forward that saved
-    the output and the row log-sum-exp.  Useful flops: 2.5 times the
+    """Time one backward step (the dq kernel, the dk/dv kernel and, for
+    split global rows and columns, the merge kernel) on the headline
+    workload's inputs, after a forward that saved the output and the row
+    log-sum-exp.  Useful flops: 2.5 times the
     forward's (the five products of the gradients; the recompute of the
     scores and the probability gradients in both kernels is not counted)."""
     w = run.w
     q, k, v, _ = run.sets[0]
     dout = torch.randn_like(q)
-    out, lse, _ = bbsa.bbsa_forward_ex(q, k, v, run.mask, run.ra, w.block, w.r, return_lse=True)
+    keep = Runner.keep_padded
+    out, lse, _ = bbsa.bbsa_forward_ex(q, k, v, run.mask, run.ra, w.block, w.r, return_lse=True,
+                                       keep_padded_blocks=keep)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     delta = torch.empty_like(lse)
 
     def step():
         bbsa.bbsa_backward(q, k, v, out, dout, lse, run.mask, run.ra, w.block, w.r, dq=dq, dk=dk, dv=dv,
-                           delta=delta, stream=run.stream)
+                           delta=delta, stream=run.stream, keep_padded_blocks=keep)
 
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < args.preroll:
@@ -339,6 +348,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--keep-padded-blocks", action="store_true",
+                    help="compute the key blocks whose keys are all padded (BBSA_FLAG_KEEP_PADDED_BLOCKS)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -362,6 +373,7 @@ def main():
         print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
         return
 
+    Runner.keep_padded = args.keep_padded_blocks
     # Headline workload.
     run = Runner(args.workload, args.sets, torch, bbsa, workloads)
     w, n_sets = run.w, run.n_sets
@@ -373,7 +385,8 @@ def main():
     roof, flops, nbytes = roofline(w, ms)
     roof["traffic"] = read_traffic(w.name)
     roof["kernel"] = "bbsa_attn_bf16" if w.dtype == "bf16" else "bbsa_attn_f32"
-    add_executed(roof, executed_pair_fraction(w, run.inp["mask"] if w.masked else None, run.plan, bbsa))
+    add_executed(roof, executed_pair_fraction(w, run.inp["mask"] if w.masked and not Runner.keep_padded else None,
+                                              run.plan, bbsa))
     # The step is one attention-kernel launch (plus the merge kernel only for
     # rows longer than 4096 keys), so the average launch duration over the
     # timed region is the step time; per-launch events (which add their own
@@ -404,7 +417,8 @@ def main():
         r2.preroll(args.preroll)
         ms2 = r2.timed(args.steps, args.warmup)
         rf2, fl2, nb2 = roofline(r2.w, ms2)
-        add_executed(rf2, executed_pair_fraction(r2.w, r2.inp["mask"] if r2.w.masked else None, r2.plan, bbsa))
+        add_executed(rf2, executed_pair_fraction(r2.w, r2.inp["mask"] if r2.w.masked and not Runner.keep_padded
+                                                 else None, r2.plan, bbsa))
         v2 = fl2 / (ms2 * 1e-3) / 1e12
         log(f"{r2.w.name}: step {ms2 * 1e3:.2f} us; {v2:.1f} useful TFLOP/s; frac {rf2['frac']} "
             f"({rf2['bound']}); MFMA {rf2['mfma_frac']} HBM {rf2['hbm_frac']}")
@@ -434,6 +448,7 @@ def main():
                    "warm_step_us": round(warm_us, 2),
                    "preroll": {"seconds": args.preroll, "steps": pre},
                    "parallelism": "none (1 GPU)",
+                   "keep_padded_blocks": bool(args.keep_padded_blocks),
                    "other_workloads": others,
                    "backward": backward},
         "roofline": roof,
