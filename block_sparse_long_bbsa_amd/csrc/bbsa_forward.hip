@@ -477,17 +477,19 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
       pr.m[u][1] = __uint_as_float(mv[1]);
     }
   };
-  // Bit t of padded: every key of position t has mask 0; valid: some key of
-  // the probed positions has mask 1.
+  // Bit t of padded: every key of position t has mask 0 (either sign); valid:
+  // the largest mask value probed is 1 (a key of mask 1 exists; values above
+  // 1 only make the test fail, which leaves every block in).
   auto probe_bits = [&](int t0, int t1, const MaskProbe &pr, uint64_t &padded, bool &valid) {
-    bool one = false;
+    float mx = 0.0f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint64_t bit = (t0 + u < t1) ? (1ull << (t0 + u)) : 0ull;
-      if (!__builtin_amdgcn_ballot_w64(pr.m[u][0] != 0.0f || pr.m[u][1] != 0.0f)) padded |= bit;
-      one |= pr.m[u][0] == 1.0f || pr.m[u][1] == 1.0f;
+      const uint32_t nz = (__float_as_uint(pr.m[u][0]) | __float_as_uint(pr.m[u][1])) << 1;
+      if (!__builtin_amdgcn_ballot_w64(nz != 0u)) padded |= bit;
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(pr.m[u][0], pr.m[u][1]));
     }
-    valid |= __builtin_amdgcn_ballot_w64(one) != 0;
+    valid |= __builtin_amdgcn_ballot_w64(mx == 1.0f) != 0;
   };
   // Drop the padded positions (stable compaction: kept position t moves to
   // the number of kept positions below it, dropped ones follow in order, a
