@@ -490,9 +490,10 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dq(BwdParams p) {
   uint64_t padded = 0;
   auto probe_bits = [&](int t0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (t0 + u < npos && !__builtin_amdgcn_ballot_w64(pm[u][0] != 0.0f || pm[u][1] != 0.0f))
-        padded |= 1ull << (t0 + u);
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t nz = (__float_as_uint(pm[u][0]) | __float_as_uint(pm[u][1])) << 1;   // 0: both are +-0
+      if (t0 + u < npos && !__builtin_amdgcn_ballot_w64(nz != 0u)) padded |= 1ull << (t0 + u);
+    }
   };
   if (compact) probe_load(0);
 
