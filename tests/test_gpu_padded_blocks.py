@@ -257,3 +257,60 @@ def test_keep_flag_covers_scores_beyond_the_padding_bias():
     out_k, _ = _run(q, k, v, mask, ra, block, r, keep=True)
     want = oracle.forward(inp["q"], inp["k"], inp["v"], m, o_plan, block)
     assert_close(out_k.float().cpu().numpy().astype(np.float64), want, "bf16", "keep flag, scores beyond the bias")
+
+
+@pytest.mark.parametrize("draw", range(10))
+def test_padded_blocks_seeded_sweep(draw):
+    """Seeded draws of shape, block size, r, query x key mode and a mask
+    with whole padded blocks, partially padded blocks and fractional values:
+    forward and backward against the oracle; the backward bit for bit
+    against computing every step, the forward bit for bit where no list
+    starts with a padded block (else to bf16 rounding)."""
+    rng = np.random.Generator(np.random.PCG64(9300 + draw))
+    block = int(rng.choice([64, 128]))
+    r = int(rng.integers(1, 6))
+    nb = int(rng.integers(6 + 2 * r, 6 + 2 * r + 14))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    L = nb * block
+    qk = bool(draw % 3 == 2)
+    seed = 9400 + draw
+    announce(f"padded sweep {draw}: B{B} H{H} L{L} b{block} r{r} qk{qk}")
+    inp = workloads.make_case(B, H, L, 64, seed, "bf16")
+    m = np.ones((B, L), np.float32)
+    for b in range(B):
+        for kb in rng.choice(np.arange(nb), size=int(rng.integers(1, nb // 2)), replace=False):
+            kind = rng.integers(0, 4)
+            lo, hi = kb * block, (kb + 1) * block
+            if kind <= 1:
+                m[b, lo:hi] = 0.0                                   # whole padded block
+            elif kind == 2:
+                m[b, lo + int(rng.integers(1, block)):hi] = 0.0     # partially padded block
+            else:
+                m[b, lo:hi] = np.float32(rng.choice([0.0, 0.25, 1.0]))
+    inp["mask"] = m
+    c_plan, o_plan = plans(H, nb, r, seed)
+    q, k, v = (to_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    mask = to_dev(m, torch.float32)
+    ra = torch.from_numpy(c_plan).cuda()
+    out, lse = _run(q, k, v, mask, ra, block, r, keep=False, qk=qk)
+    out_k, lse_k = _run(q, k, v, mask, ra, block, r, keep=True, qk=qk)
+    want = oracle.forward(inp["q"], inp["k"], inp["v"], m, o_plan, block, query_key_mask=qk)
+    assert_close(out.float().cpu().numpy().astype(np.float64), want, "bf16", f"padded sweep {draw} forward")
+    first = _first_blocks(H, L, block, r, c_plan)
+    blocks = m.reshape(B, nb, block)
+    if not any((blocks[:, f] == 0).all() for f in first):
+        assert torch.equal(out, out_k) and torch.equal(lse, lse_k), "forward: skip and keep differ"
+    else:
+        assert float((out.float() - out_k.float()).abs().max()) <= 1.6e-2
+    dout_np = workloads.round_to_bf16(rng.standard_normal((B, H, L, 64)).astype(np.float32))
+    dout = to_dev(dout_np, torch.bfloat16)
+    got, ref = _backward(q, k, v, dout, mask, ra, block, r, qk=qk)
+    for name, g, w in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.isfinite(g.float()).all(), f"{name}: unwritten entries"
+        assert torch.equal(g, w), f"{name}: skipping padded steps changed the gradient"
+    want_g = oracle.backward(inp["q"], inp["k"], inp["v"], m, o_plan, block, dout_np, query_key_mask=qk)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want_g):
+        g = g.float().cpu().numpy().astype(np.float64)
+        s = max(1.0, float(np.abs(w).max()))
+        err = np.abs(g - w)
+        assert err.max() <= 2e-2 * s and err.mean() <= 2e-3 * s, f"{name}: max abs {err.max()} (scale {s})"
