@@ -45,6 +45,9 @@ constexpr int kF32SmallParts = 4;
 constexpr int kPartialFloats = kQT * kD + 2 * kQT + 4;
 constexpr int kMergeSlices = kQT / 4;   // merge-kernel workgroups per row tile
 constexpr int kMaxL = 1 << 24;          // longest supported sequence (tokens)
+// Wavefront slots of the bf16 attention kernel on MI355X: 256 CUs, two
+// four-wavefront workgroups each.
+constexpr int64_t kBf16Slots = 2048;
 
 // Division of 31-bit non-negative integers by a divisor fixed at launch:
 // q = (mulhi(n, m) + n) >> s with s = ceil(log2 d) and
@@ -259,12 +262,23 @@ inline int setup_forward_ex(const void *q, const void *k, const void *v, const f
   p.skip_padded = (mask && !ragged && dtype == BBSA_BF16 && !(flags & BBSA_FLAG_KEEP_PADDED_BLOCKS)) ? 1 : 0;
   p.qtiles = block / kQT;
   p.n_rows_global = full ? nb : 2;
-  // Full rows are cut into chunks of about 1024 keys (bf16) or 256 keys (the
-  // slower fp32 path) so they do not form the tail.  On the bf16 path the
-  // chunk count is a multiple of kGroup: each workgroup runs kGroup chunks
-  // of one row tile and merges them in LDS, and the merge kernel combines
-  // the chunks / kGroup group results (none for rows of up to 4096 keys).
-  int per_chunk = (dtype == BBSA_F32 ? 256 : 1024) / block;   // blocks
+  // Full rows are cut into chunks so they do not form the tail: 256 keys on
+  // the slower fp32 path; on the bf16 path 1024, 2048 or 4096 keys, the
+  // longest whose 32-key steps stay within one wavefront slot's share of
+  // the launch's steps (kBf16Slots slots), since longer chunks leave fewer
+  // partials to merge.  On the bf16 path the chunk count is a multiple of
+  // kGroup: each workgroup runs kGroup chunks of one row tile and merges
+  // them in LDS, and the merge kernel combines the chunks / kGroup group
+  // results (none for rows of up to 4 chunks).
+  int per_chunk = 256 / block;   // blocks
+  if (dtype == BBSA_BF16) {
+    const int64_t spb = block / kStep;
+    const int64_t steps = bh * p.qtiles * spb *
+                          ((int64_t)p.n_rows_global * nb + (full ? 0 : (int64_t)(nb - 2) * (5 + r)));
+    int keys = 1024;
+    while (keys < 4096 && 2 * keys / kStep <= steps / kBf16Slots) keys *= 2;
+    per_chunk = keys / block;
+  }
   bool f32_small = false;
   if (dtype == BBSA_F32 && !full) {
     const int64_t items = bh * p.qtiles * (2 * (int64_t)((nb + per_chunk - 1) / per_chunk) + (nb - 2));

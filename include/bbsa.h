@@ -166,8 +166,8 @@ int bbsa_truncate_rand_attn(const int32_t *src, int H, int nb_src, int r, int32_
  * Limits (BBSA_ERR_UNSUPPORTED beyond them): d = 64; block 64 or 128;
  * on the sparse path 5 + r <= 64 (a middle row attends at most 64 key
  * blocks); L <= 2^24; B * H * L * d <= 2^40 elements; at most 2^31 - 1
- * workgroups; (key chunks per full row) * nb < 2^31, i.e. about
- * L <= 11.8 million tokens for bf16 with block 64.
+ * workgroups; (key chunks per full row) * nb < 2^31, which binds only the
+ * fp32 path (256-key chunks: about L <= 5.9 million tokens with block 64).
  *
  * Returns BBSA_OK, or BBSA_OK_FULL_FALLBACK when L <= (5 + 2r) * block (every
  * query block then attends every key block), or a negative error code.  All
@@ -312,7 +312,9 @@ int bbsa_backward(const void *q, const void *k, const void *v, const void *out, 
  * fixed 16 MiB array that the library holds on each device it runs on until
  * the process ends, so the call itself allocates nothing.  That fits 1007
  * partials of 16.3 KiB: every bf16 call with L <= 4096 (none needed), and
- * e.g. B * H * 2 * (L / 4096) <= 1007 bf16 row tiles of block 64.  A call
+ * in general B * H * 2 * (block / 64) * ceil(L / (4 c)) <= 1007, where c is
+ * the full-row chunk length: 1024, 2048 or 4096 keys, longer for launches
+ * with more work (4096 at B 8, H 16, L 32768).  A call
  * needing more returns BBSA_ERR_SCRATCH before any HIP call.  Every call on
  * one GPU shares that GPU's array: calls that overlap on one GPU (different
  * streams, or different host threads) race and must be ordered by the

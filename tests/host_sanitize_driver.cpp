@@ -77,9 +77,10 @@ static void validation() {
       {INT_MAX, INT_MAX, INT_MAX - 63, 64, 64, 3, BBSA_BF16, BBSA_ERR_UNSUPPORTED},
       {INT_MAX, INT_MAX, 1 << 20, 64, 64, 3, BBSA_BF16, BBSA_ERR_UNSUPPORTED},
       {1, 1, (1 << 24) + 64, 64, 64, 3, BBSA_BF16, BBSA_ERR_UNSUPPORTED},
-      {1, 1, 1 << 24, 64, 64, 3, BBSA_BF16, BBSA_ERR_UNSUPPORTED},   // chunks * nb >= 2^31
+      {1, 1, 1 << 24, 64, 64, 3, BBSA_BF16, BBSA_OK},   // 4096-key chunks: chunks * nb = 2^30
       {1, 1, 11 << 20, 64, 64, 3, BBSA_BF16, BBSA_OK},
-      {1, 1, 1 << 23, 64, 64, 3, BBSA_F32, BBSA_ERR_UNSUPPORTED},
+      {1, 1, 1 << 23, 64, 64, 3, BBSA_F32, BBSA_ERR_UNSUPPORTED},   // 256-key chunks: chunks * nb = 2^32
+      {1, 1, 5 << 20, 64, 64, 3, BBSA_F32, BBSA_OK},
       {1, 1, INT_MAX, 64, 64, INT_MAX, BBSA_BF16, BBSA_ERR_SHAPE},
       {1, 1, 1 << 20, 64, 128, INT_MAX / 128, BBSA_BF16, BBSA_OK_FULL_FALLBACK},
   };
@@ -104,8 +105,10 @@ static void validation() {
         BBSA_ERR_ARG);
   CHECK(setup_forward_ex(P, P, P, nullptr, nullptr, 1, 1, 700, 64, 64, 3, P, nullptr, 0, 1u, &ln) ==
         BBSA_OK_FULL_FALLBACK);
-  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, (1 << 24) - 1, 64, 64, 3, P, nullptr, 0, 1u, &ln) ==
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, (1 << 23) - 1, 64, 64, 3, P, nullptr, BBSA_F32, 1u, &ln) ==
         BBSA_ERR_UNSUPPORTED);   // chunks * nb >= 2^31
+  CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, (1 << 24) - 1, 64, 64, 3, P, nullptr, 0, 1u, &ln) == BBSA_OK);
+  CHECK(ln.p.chunks * ln.p.nb == (1 << 30));
   CHECK(setup_forward_ex(P, P, P, nullptr, ra, 1, 1, (1 << 24) + 1, 64, 64, 3, P, nullptr, 0, 1u, &ln) ==
         BBSA_ERR_UNSUPPORTED);   // L > 2^24
   // Null and misaligned pointers.

@@ -84,7 +84,7 @@ def test_noalloc_validates_like_forward(lib):
                                       args["H"], args["L"], args["d"], args["block"], args["r"], args["out"],
                                       None, args["dtype"])
         assert st == code
-    st = lib.bbsa_forward_noalloc(FAKE, FAKE, FAKE, None, FAKE, 8, 16, 32768, 64, 64, 3, FAKE, None, 0)
+    st = lib.bbsa_forward_noalloc(FAKE, FAKE, FAKE, None, FAKE, 64, 16, 32768, 64, 64, 3, FAKE, None, 0)
     assert st == bbsa.BBSA_ERR_SCRATCH
 
 

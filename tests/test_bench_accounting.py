@@ -80,7 +80,7 @@ def _executed_by_rows(w, mask, plan, chunks):
     return executed / total
 
 
-@pytest.mark.parametrize("wid,chunks", [(2, 4), (3, 4), (4, 16), (5, 32)])
+@pytest.mark.parametrize("wid,chunks", [(2, 4), (3, 4), (4, 16), (5, 8)])
 def test_executed_pair_fraction(wid, chunks):
     """bench.executed_pair_fraction (the library's work map plus the mask)
     against the same rule applied to the pattern's block mask."""

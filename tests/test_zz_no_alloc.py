@@ -78,9 +78,15 @@ def test_noalloc_on_a_side_stream():
 
 
 def test_noalloc_refuses_more_than_its_scratch():
-    # 8 x 16 pairs of 32768-token rows need 2048 partials (> 1007): refused
-    # during validation, before any HIP call (the pointers are never used).
+    # 64 x 16 pairs of 32768-token rows: even with the longest full-row chunks
+    # (4096 keys, 4 per partial) the two global row tiles of each pair need
+    # 2 * ceil(32768 / 16384) partials, 4096 in all (> 1007), so the call is
+    # refused during validation, before any HIP call; the pointers are never
+    # used.  The count is checked here first: a shape that fitted would launch
+    # kernels on the fake pointers.
+    B, H, L, block = 64, 16, 32768, 64
+    assert B * H * 2 * (block // 64) * -(-L // (4 * 4096)) > 1007
     fake = ctypes.c_void_p(0x10000)
-    st = bbsa.lib().bbsa_forward_noalloc(fake, fake, fake, None, fake, 8, 16, 32768, 64, 64, 3, fake, None,
+    st = bbsa.lib().bbsa_forward_noalloc(fake, fake, fake, None, fake, B, H, L, 64, block, 3, fake, None,
                                          bbsa.BBSA_BF16)
     assert st == bbsa.BBSA_ERR_SCRATCH
