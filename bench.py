@@ -38,7 +38,8 @@ METRIC = "block-sparse attn fwd TFLOP/s (useful) + % MFMA/HBM roofline, L=4096 H
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (no sparsity)
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 MFMA
-KERNEL_SOURCES = ["block_sparse_long_bbsa_amd/csrc/bbsa_forward.hip"]
+# The kernel and the host code that decides its work decomposition.
+KERNEL_SOURCES = ["block_sparse_long_bbsa_amd/csrc/bbsa_forward.hip", "block_sparse_long_bbsa_amd/csrc/bbsa_schedule.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bbsa_attn_bf16_B4_H12_L4096.json")
 
 
