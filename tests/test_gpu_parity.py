@@ -65,6 +65,43 @@ def test_f32_large_call_without_middle_split():
     want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64, query_blocks=blocks)
     assert_close(gather_rows(got, blocks, 64), want, "f32", "f32 no split")
 
+# The full-row chunk length grows with the launch's work (1024, 2048 or
+# 4096 keys); four chunks share a workgroup and merge in LDS, more leave
+# partials for the merge kernel.  One case per length and merge path, padded
+# so that whole chunks of the global rows lie in the padding.
+CHUNK_CASES = [
+    # B, H, L, r, expected (chunk blocks, chunks per full row), valid lengths
+    (8, 16, 8192, 3, (32, 4), (8192, 7000, 6500, 8192, 4000, 8000, 7777, 6144)),
+    (2, 16, 16384, 3, (32, 8), (16384, 9000)),
+    (4, 16, 16384, 3, (64, 4), (16384, 12000, 3000, 15999)),
+    (4, 16, 32768, 3, (64, 8), (32768, 20000, 30001, 9000)),
+]
+
+
+@pytest.mark.parametrize("B,H,L,r,chunking,valid", CHUNK_CASES)
+def test_full_row_chunk_lengths(B, H, L, r, chunking, valid):
+    block, nb, seed = 64, L // 64, 21
+    announce(f"chunk lengths B{B} H{H} L{L} r{r} chunking {chunking}")
+    cplan, oplan = plans(H, nb, r, seed)
+    st, _, rec = bbsa.bbsa_work_map(B, H, L, 64, block, r, bbsa.BBSA_BF16, cplan)
+    glob = rec[rec[:, 6] >= 0]
+    assert st == bbsa.BBSA_OK and (glob[:, 11] == chunking[1]).all()
+    assert ((glob[:, 9] - glob[:, 8]) == chunking[0]).all()
+    inp = workloads.make_case(B, H, L, 64, seed, valid=valid)
+    got, st = run_gpu(inp, block, r, "bf16", cplan)
+    assert st == bbsa.BBSA_OK
+    assert np.isfinite(got).all(), "non-finite output: some row was not written"
+    # Both global rows and two middle rows of one pair per XCD lane and of
+    # the last pair.
+    jobs = []
+    for bh in sorted(set(list(range(min(8, B * H))) + [B * H - 1])):
+        b, h = divmod(bh, H)
+        jobs.append((b, h, [0, 1 + bh % (nb - 2), nb // 2, nb - 1]))
+    wants = oracle_slices(inp, oplan, block, jobs)
+    g = np.concatenate([gather_rows(got[b, h], qbs, block) for b, h, qbs in jobs])
+    assert_close(g, np.concatenate(wants), "bf16", f"chunks B{B} H{H} L{L}")
+
+
 FALLBACK = [
     (1, 2, 704, 64, 3, "bf16", (650,)),    # (5 + 2*3) * 64 = 704: full attention
     (2, 1, 1152, 128, 2, "bf16", None),    # (5 + 2*2) * 128
