@@ -389,7 +389,7 @@ def main():
     add_executed(roof, executed_pair_fraction(w, run.inp["mask"] if w.masked and not Runner.keep_padded else None,
                                               run.plan, bbsa))
     # The step is one attention-kernel launch (plus the merge kernel only for
-    # rows longer than 4096 keys), so the average launch duration over the
+    # rows of more than four key chunks), so the average launch duration over the
     # timed region is the step time; per-launch events (which add their own
     # overhead) are reported beside it.
     roof["kernel_us"] = round(ms * 1e3, 3)

@@ -173,7 +173,8 @@ int bbsa_truncate_rand_attn(const int32_t *src, int H, int nb_src, int r, int32_
  * query block then attends every key block), or a negative error code.  All
  * argument checks happen before any HIP call.
  *
- * Workspace: rows that leave more than one split-K partial (bf16 rows longer
+ * Workspace: rows that leave more than one split-K partial (bf16 rows of
+ * more than four key chunks of 1024 to 4096 keys, so only some rows longer
  * than 4096 keys; fp32 rows longer than 256 keys, and in fp32 calls with
  * fewer than 2048 wavefronts of work full rows longer than 128 keys and
  * every middle row) use a library-owned workspace, one per (device, stream).
