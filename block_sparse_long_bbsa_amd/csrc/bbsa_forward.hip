@@ -511,10 +511,12 @@ __global__ __launch_bounds__(kGroup * 64, 2) void bbsa_attn_bf16(Params p) {
   // K and V of this (batch, head) as buffer resources (L x d rows): the DMA
   // source of a lane is a 32-bit per-lane offset plus a scalar offset for the
   // step.
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Kbh, (short)0, p.L * kD * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Vbh, (short)0, p.L * kD * 2, kBufferWord3);
+  // The record count is an unsigned 32-bit byte count: L * 128 reaches 2^31
+  // at the longest supported L, so it is formed in 64 bits and passed as its
+  // low 32 bits.
+  const int kv_bytes = (int)(uint32_t)(p.seq_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kbh, (short)0, kv_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vbh, (short)0, kv_bytes, kBufferWord3);
   // The instruction offset 1024u moves both the LDS destination and the
   // source by 1024u bytes: one M0 value per tile.
   int kdma_b[4];

@@ -4,7 +4,10 @@ This module holds no attention arithmetic and no planner: it only draws the
 inputs (Q, K, V, padding mask) that both the HIP path and the CPU oracle
 consume, so that both sides see exactly the same numbers.  The random-block
 plan is *not* drawn here; each side builds it from the plan seed with its
-own SplitMix64 planner.
+own SplitMix64 planner.  The one exception is ``block_constant_case``, for
+lengths where the oracle planner's per-row candidate lists do not fit in
+memory: it draws an arbitrary plan that satisfies the plan invariants (not
+the method's planner) and passes it to both sides as an input.
 
 The five workloads stand in for the encoder shapes the pages describe
 (BigBird-base: 12 heads of 64 on hidden 768, block 64, 3 random blocks;
@@ -130,3 +133,37 @@ def make_case(B, H, L, d, seed, dtype="bf16", valid=None, q_scale=None):
         valid = np.asarray(valid)
         mask = (np.arange(L)[None, :] < valid[:, None]).astype(np.float32)
     return {"q": q, "k": k, "v": v, "mask": mask}
+
+
+def block_constant_case(L, d, block, r, seed, valid):
+    """Inputs constant over each key block, for checks at lengths whose dense
+    oracle does not fit in memory (one batch, one head).
+
+    Every query row is the unit vector e_0, so a key's score is component 0
+    of its key vector.  Key and value vectors are drawn per block (float32
+    ``standard_normal``, keys times 2, rounded to bfloat16) and repeated over
+    the block's rows.  The mask is 1 on the first ``valid`` positions.  The
+    plan ``[1, nb - 2, r]`` holds, for every middle row, r distinct middle
+    blocks outside the row's window, drawn uniformly with redraws of entries
+    that break this; it is an input like the others, not the method's
+    planner.  Returns block-level ``k_blocks``, ``v_blocks`` (``[nb, d]``),
+    ``mask`` (``[1, L]``) and ``plan``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nb = L // block
+    kb = round_to_bf16(2.0 * rng.standard_normal((nb, d), dtype=np.float32))
+    vb = round_to_bf16(rng.standard_normal((nb, d), dtype=np.float32))
+    rows = np.arange(1, nb - 1)[:, None]
+    plan = rng.integers(1, nb - 1, size=(nb - 2, r))
+
+    def bad(pl):
+        out = np.abs(pl - rows) <= 1
+        for t in range(1, r):
+            out[:, t] |= (pl[:, :t] == pl[:, t:t + 1]).any(axis=1)
+        return out
+
+    b = bad(plan)
+    while b.any():
+        plan[b] = rng.integers(1, nb - 1, size=int(b.sum()))
+        b = bad(plan)
+    mask = (np.arange(L)[None, :] < valid).astype(np.float32)
+    return {"k_blocks": kb, "v_blocks": vb, "mask": mask, "plan": plan.astype(np.int32)[None]}

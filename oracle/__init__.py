@@ -23,7 +23,8 @@ from .planner import (SplitMix64, plan_rand_attn, check_rand_attn, candidate_blo
                       truncate_plan)
 from .attention import (
     block_mask, token_mask, key_bias, uses_full_fallback, forward, full_attention,
-    attended_key_counts, pair_bias, forward_padded, backward, backward_padded,
+    attended_key_counts, pair_bias, forward_padded, backward, backward_padded, attended_blocks,
+    forward_block_constant,
 )
 
 __all__ = [
@@ -31,5 +32,5 @@ __all__ = [
     "truncate_plan",
     "block_mask", "token_mask", "key_bias", "uses_full_fallback", "forward",
     "full_attention", "attended_key_counts", "pair_bias", "forward_padded",
-    "backward", "backward_padded",
+    "backward", "backward_padded", "attended_blocks", "forward_block_constant",
 ]

@@ -41,12 +41,14 @@ Readings where the pages are silent:
   the page's text; 704 = (5 + 2*3) * 64 confirms it).
 
 Also: the query x key masking mode (the pages' band mask is the outer
-product of the query-side and key-side masks), each row's log-sum-exp, and
+product of the query-side and key-side masks), each row's log-sum-exp,
 lengths that are not a multiple of the block (the encoder pads to the block
-and trims the output).
+and trims the output), and the output for inputs constant over each key
+block one query block at a time (for lengths whose dense scores do not fit
+in memory).
 
 Parity status: pinned (tests/test_oracle_attention.py,
-tests/test_oracle_extensions.py) against scalar brute force on tiny inputs,
+tests/test_oracle_extensions.py, tests/test_oracle_block_constant.py) against scalar brute force on tiny inputs,
 against torch's scaled_dot_product_attention and logsumexp in float64,
 against closed forms (constant V, Q = 0, key shift, attended-key counts,
 query x key rows with mask 1 or 0) and against invariants (row sums, exact
@@ -303,4 +305,52 @@ def full_attention(q, k, v, mask):
         for h in range(H):
             S = q[b, h] @ k[b, h].T + bias[b][None, :]
             out[b, h] = _softmax_rows(S) @ v[b, h]
+    return out
+
+
+def attended_blocks(nb: int, i: int, rand_attn_h) -> np.ndarray:
+    """The key blocks query block ``i`` sees, ascending and distinct: the
+    row of ``block_mask`` taken on its own, for sequences whose ``[nb, nb]``
+    mask does not fit in memory.  The global blocks 0 and nb-1 see every
+    block; a middle block sees blocks 0 and nb-1, its window i-1..i+1 and
+    its random blocks (row i-1 of ``rand_attn_h``)."""
+    if i == 0 or i == nb - 1:
+        return np.arange(nb)
+    seen = {0, nb - 1, i - 1, i, i + 1}
+    if rand_attn_h is not None:
+        seen.update(int(j) for j in np.asarray(rand_attn_h)[i - 1])
+    return np.array(sorted(seen))
+
+
+def forward_block_constant(k_blocks, v_blocks, mask_b, rand_attn_h, block: int, query_blocks, query=None):
+    """``forward`` of one (batch, head) whose query rows all equal ``query``
+    (default: the unit vector e_0) and whose key and value rows are constant
+    over each key block: row u of K is ``k_blocks[u // block]``, row u of V
+    is ``v_blocks[u // block]``.  For lengths whose dense scores do not fit
+    in memory; no fallback (the sequence must be longer than the fallback
+    threshold).
+
+    The definition as in ``forward``, with its sums regrouped: key u of block
+    b scores query . k_b plus the key bias -10000 (1 - m_u), the row softmax
+    runs over the keys of the attended blocks, and since every key of block
+    b carries v_b the output is sum_b (sum of the probabilities of block b's
+    keys) v_b.  All rows of a query block are equal; returns float64
+    ``[len(query_blocks), d]``, one row per query block."""
+    kb = np.asarray(k_blocks, dtype=np.float64)
+    vb = np.asarray(v_blocks, dtype=np.float64)
+    nb, d = kb.shape
+    L = nb * block
+    qv = np.zeros(d) if query is None else np.asarray(query, dtype=np.float64)
+    if query is None:
+        qv[0] = 1.0
+    m = np.ones(L) if mask_b is None else np.asarray(mask_b, dtype=np.float64).reshape(L)
+    block_scores = kb @ qv                                      # [nb]
+    out = np.empty((len(query_blocks), d), dtype=np.float64)
+    for n, i in enumerate(query_blocks):
+        A = attended_blocks(nb, int(i), rand_attn_h)
+        tok = (A[:, None] * block + np.arange(block)[None, :]).ravel()
+        S = np.repeat(block_scores[A], block) + PAD_BIAS * (1.0 - m[tok])
+        P = np.exp(S - S.max())
+        P /= P.sum()
+        out[n] = P.reshape(len(A), block).sum(axis=1) @ vb[A]
     return out

@@ -159,3 +159,40 @@ def test_two_streams_with_workspace_run_concurrently():
     for (inp, oplan, dev), o in zip(cases, outs):
         want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["mask"], oplan, 64)
         assert_close(o.float().cpu().numpy().astype(np.float64), want, "bf16", "two streams")
+
+
+def test_longest_sequence_block_constant_inputs():
+    # L = 2^24, the longest supported length: every offset at its largest
+    # (K and V byte ranges of 2^31, 4096 key chunks per global row, 2048
+    # split-K partials).  Its dense oracle does not fit in memory, so the
+    # inputs are constant over each key block (query rows e_0) and the
+    # oracle's closed form for such inputs gives the expected rows: both
+    # global rows, their neighbours, rows whose window meets the padding,
+    # and middle rows drawn at random.  The padding covers the last 1000
+    # positions (a partial block, then 15 whole padded blocks).
+    L, block, r, d = 1 << 24, 64, 3, 64
+    nb = L // block
+    announce(f"longest sequence B1 H1 L{L} block{block} r{r}")
+    case = workloads.block_constant_case(L, d, block, r, seed=41, valid=L - 1000)
+    dev = torch.device("cuda:0")
+    kb = torch.from_numpy(case["k_blocks"]).to(torch.bfloat16).to(dev)
+    vb = torch.from_numpy(case["v_blocks"]).to(torch.bfloat16).to(dev)
+    k = kb.repeat_interleave(block, dim=0).view(1, 1, L, d)
+    v = vb.repeat_interleave(block, dim=0).view(1, 1, L, d)
+    q = torch.zeros((1, 1, L, d), dtype=torch.bfloat16, device=dev)
+    q[..., 0] = 1.0
+    mask = torch.from_numpy(case["mask"]).to(dev)
+    ra = torch.from_numpy(case["plan"]).to(dev)
+    out = torch.full_like(q, float("nan"))
+    out, st = bbsa.bbsa_forward(q, k, v, mask, ra, block, r, out=out)
+    torch.cuda.synchronize()
+    assert st == bbsa.BBSA_OK
+    assert bool(torch.isfinite(out).all()), "non-finite output: some row was not written"
+    rng = np.random.Generator(np.random.PCG64(42))
+    extra = [int(x) for x in rng.choice(np.arange(2, nb - 2), size=8, replace=False)]
+    qbs = sorted(set([0, 1, 2, nb // 2, nb - 18, nb - 17, nb - 16, nb - 15, nb - 2, nb - 1] + extra))
+    got = out[0, 0].view(nb, block, d)[torch.tensor(qbs, device=dev)].float().cpu().numpy().astype(np.float64)
+    del q, k, v, out
+    want = oracle.forward_block_constant(case["k_blocks"], case["v_blocks"], case["mask"][0], case["plan"][0],
+                                         block, qbs)
+    assert_close(got, np.repeat(want[:, None, :], block, axis=1), "bf16", f"longest L{L}")
