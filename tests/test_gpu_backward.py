@@ -161,6 +161,29 @@ def test_backward_pegasus_workload():
         check([g[sl] for g in got], want, f"backward {w.name} pair {bh}")
 
 
+@pytest.mark.parametrize("wid,bh", [(4, 9), (5, 15)])
+def test_backward_long_workloads(wid, bh):
+    # The 16384-token workload (no mask; global rows and columns in four
+    # chunks) and the 32768-token block-128 workload (padded tail, key
+    # outliers, two 64-query tiles per block) through the backward; every
+    # gradient row of one (batch, head) pair on an XCD lane other than 0.
+    w = workloads.WORKLOADS[wid]
+    announce(f"backward workload {wid} {w.name} pair {bh}")
+    inp = workloads.make_inputs(wid)
+    rng = np.random.Generator(np.random.PCG64(404 + wid))
+    dout = bf16_exact(rng.standard_normal(inp["q"].shape).astype(np.float32))
+    cplan, oplan = plans(w.H, w.nb, w.r, w.plan_seed)
+    got, st = run_backward(inp, dout, w.block, w.r, cplan, no_mask=not w.masked)
+    assert st == bbsa.BBSA_OK
+    for g in got:
+        assert np.isfinite(g).all()
+    b, h = divmod(bh, w.H)
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    want = oracle.backward(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["mask"][b:b + 1] if w.masked else None,
+                           oplan[h:h + 1], w.block, dout[sl])
+    check([g[sl] for g in got], want, f"backward {w.name} pair {bh}")
+
+
 F32_CASES = [
     # B, H, L, block, r, valid, pad, qk, seed
     (1, 2, 1024, 64, 3, (1024,), False, False, 21),       # the fp32 workload's shape
