@@ -140,3 +140,36 @@ def test_work_map_random_shapes(lib, seed):
     if L > (5 + 2 * r) * block and nb < 5 + r:
         return
     _check(B, H, L, block, r, dtype)
+
+
+@pytest.mark.parametrize("B,H,L,block,r", [
+    (1, 1, 1024, 64, 3), (4, 12, 4096, 64, 3), (8, 16, 4096, 64, 3), (2, 12, 16384, 64, 3),
+    (2, 16, 16384, 64, 3), (4, 16, 16384, 64, 3), (1, 16, 32768, 128, 2), (8, 16, 8192, 64, 3),
+    (1, 1, 1 << 20, 64, 3), (3, 5, 65536, 128, 7), (64, 16, 4096, 64, 3),
+])
+def test_bf16_full_row_chunk_length(lib, B, H, L, block, r):
+    # bf16 full rows are cut into chunks of 1024, 2048 or 4096 keys, as many
+    # as a multiple of four (four chunks share a workgroup; a row of at most
+    # four chunks is cut into four shorter ones).  A chunk longer than 1024
+    # keys fits in one wavefront slot's share of the launch's 32-key steps
+    # (2048 slots); a row of more than four chunks uses the longest length
+    # that fits.
+    nb = L // block
+    plan = bbsa.bbsa_plan_rand_attn(H, nb, r, 3)
+    st, grid, rec = bbsa.bbsa_work_map(B, H, L, 64, block, r, bbsa.BBSA_BF16, plan)
+    assert st == bbsa.BBSA_OK
+    steps = sum(int(x[9] - x[8]) * int(x[10]) for x in rec)
+    share = steps / 2048
+    glob = rec[rec[:, 6] >= 0]
+    chunks = int(glob[0, 11])
+    assert (glob[:, 11] == chunks).all() and chunks % 4 == 0
+    keys = max(int(x[9] - x[8]) for x in glob) * block
+    if keys > 1024:
+        assert keys // 32 <= share
+    if chunks > 4:
+        assert keys in (1024, 2048, 4096)
+        assert chunks == 4 * -(-nb // (4 * (keys // block)))
+        if keys < 4096:
+            assert 2 * keys // 32 > share
+    else:
+        assert keys == -(-nb // 4) * block
