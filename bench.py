@@ -26,7 +26,9 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -284,6 +286,43 @@ class Runner:
         bbsa.bbsa_timing_enable(False)
         return main_ms / max(calls, 1) * 1e3, comb_ms / max(calls, 1) * 1e3
 
+    def clock_under_load(self, seconds):
+        """Mean graphics clock (MHz) that ``amd-smi metric -c`` reports for the
+        GPU while this workload's steps run back to back for ``seconds``
+        (untimed), with the number of readings; None when the tool is missing,
+        fails or lists more than one GPU."""
+        torch = self.torch
+        readings, stop = [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    res = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                                         timeout=10)
+                    gpus = json.loads(res.stdout)["gpu_data"]
+                    if len(gpus) != 1:
+                        return
+                    clk = [v["clk"]["value"] for k, v in gpus[0]["clock"].items() if k.startswith("gfx_")]
+                    readings.append(sum(clk) / len(clk))
+                except (OSError, ValueError, KeyError, TypeError, ZeroDivisionError, subprocess.SubprocessError):
+                    return
+                stop.wait(0.05)
+
+        th = threading.Thread(target=sample, daemon=True)
+        t0, i = time.perf_counter(), 0
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(64):
+                self.step(i)
+                i += 1
+            torch.cuda.synchronize()
+        stop.set()
+        th.join(timeout=15)
+        if not readings:
+            return None
+        return {"mhz": round(float(np.mean(readings)), 1), "readings": len(readings),
+                "tool": "amd-smi metric -c (mean of the gfx_* clocks)"}
+
     def close(self):
         self.sets = None
         self.torch.cuda.synchronize()
@@ -347,6 +386,8 @@ def main():
     ap.add_argument("--preroll", type=float, default=0.3,
                     help="seconds of untimed steps before each workload's warm-up (clock ramp)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
+    ap.add_argument("--clock-seconds", type=float, default=1.0,
+                    help="seconds of untimed steps while amd-smi reads the graphics clock (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--keep-padded-blocks", action="store_true",
@@ -394,6 +435,9 @@ def main():
     # overhead) are reported beside it.
     roof["kernel_us"] = round(ms * 1e3, 3)
     roof["per_launch_event_us"] = {"attention": round(kern_us, 3), "merge": round(merge_us, 3)}
+    # The peaks assume the 2.4 GHz specification clock; the graphics clock
+    # that amd-smi reports while the same steps run on (untimed).
+    roof["amd_smi_gfx_clock"] = run.clock_under_load(args.clock_seconds) if args.clock_seconds > 0 else None
     value = flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: step {ms * 1e3:.2f} us (p10/p50/p90 {p10}/{p50}/{p90}, warm {warm_us:.1f}); "
         f"{value:.1f} useful TFLOP/s; frac {roof['frac']} ({roof['bound']}); "
