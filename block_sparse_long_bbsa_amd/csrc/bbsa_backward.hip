@@ -14,7 +14,7 @@
 //
 // Kernels:
 //   * bbsa_bwd_dq: one wavefront per 32-query tile, walking the tile's key
-//     blocks (the forward's list; a chunk of every block for a global row)
+//     blocks (the forward's blocks; a chunk of every block for a global row)
 //     32 keys at a time: S^T = K Q^T and dP^T = V dO^T on MFMA 32x32x16
 //     bf16 (Q and dO in registers, K and V rows from LDS), dS^T = P^T (dP^T
 //     - D) in registers, then dQ^T += K^T dS^T (K read transposed from
@@ -322,8 +322,9 @@ __device__ inline void wait_step() {
 }
 __device__ inline void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Key block of list position t of middle query block i (the forward's list:
-// the two global blocks, the window without them, the plan's blocks).
+// Key block of list position t of middle query block i (the forward's blocks:
+// the two global blocks, the window without them in ascending order, the
+// plan's blocks).
 __device__ inline int list_block(const BwdParams &p, const int32_t *plan_row, int i, int t) {
   if (t == 0) return 0;
   if (t == 1) return p.nb - 1;

@@ -59,9 +59,10 @@ __device__ inline float mask_at(const F32Params &p, const float *mrow, int pos) 
   return pos < p.L ? (mrow ? mrow[pos] : 1.0f) : 0.0f;
 }
 
-// Length of query block i's key list, and its entry t (the forward's list:
+// Length of query block i's key list, and its entry t (the forward's blocks:
 // every block for a global row or on the fallback; else the two global
-// blocks, the window without them, the plan's blocks, clamped).
+// blocks, the window without them in ascending order, the plan's blocks,
+// clamped).
 __device__ inline int list_len(const F32Params &p, int i) {
   if (p.full || i == 0 || i == p.nb - 1) return p.nb;
   return 2 + ((i == 1 || i == p.nb - 2) ? 2 : 3) + p.r;

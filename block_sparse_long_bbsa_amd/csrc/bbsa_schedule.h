@@ -172,7 +172,11 @@ struct KeyWalk {
 // rslot is the lane's slot in the plan row, -1 if none); merge_plan puts the
 // random blocks in, clamped to [0, nb) so that a bad plan never reads outside
 // the sequence.  A middle row lists the two global blocks, its window without
-// them, then its random blocks; a full-row chunk lists its block range.
+// them, then its random blocks; a full-row chunk lists its block range.  A
+// three-block window is listed by block index mod 3: the four consecutive
+// query blocks of a workgroup have overlapping windows, and this order puts
+// a block they share at the same list position, so their wavefronts fetch
+// it at the same step and the later fetches find it in the caches.
 __host__ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int lane, int &rnd,
                                                   int &rslot) {
   KeyWalk w;
@@ -196,7 +200,7 @@ __host__ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &i
     rslot = (t >= 0 && t < p.r) ? t : -1;
     blk = 0;
     if (lane == 1) blk = p.nb - 1;
-    else if (lane >= 2 && lane < 2 + nw) blk = w0 + (lane - 2);
+    else if (lane >= 2 && lane < 2 + nw) blk = (nw == 3) ? (i - 1) + ((lane - 2) - (i - 1) % 3 + 3) % 3 : w0 + (lane - 2);
   } else {
     blk = first + std::max(std::min(lane, nblk - 1), 0);
   }
