@@ -172,7 +172,8 @@ struct KeyWalk {
 // rslot is the lane's slot in the plan row, -1 if none); merge_plan puts the
 // random blocks in, clamped to [0, nb) so that a bad plan never reads outside
 // the sequence.  A middle row lists the two global blocks, its window without
-// them, then its random blocks; a full-row chunk lists its block range.  A
+// them, then its random blocks; a full-row chunk lists every p.group-th block
+// of its group's range (below).  A
 // three-block window is listed by block index mod 3: the four consecutive
 // query blocks of a workgroup have overlapping windows, and this order puts
 // a block they share at the same list position, so their wavefronts fetch
@@ -184,8 +185,16 @@ __host__ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &i
   const bool middle = it.grow < 0;
   const int i = it.qblock;
   const int nw = (i == 1 || i == p.nb - 2) ? 2 : 3;
-  const int first = fdiv(it.chunk * p.nb, p.div_chunks);
-  const int nblk = middle ? 2 + nw + p.r : fdiv((it.chunk + 1) * p.nb, p.div_chunks) - first;   // may be 0 if nb < chunks
+  // A full-row chunk: the p.group chunks of a workgroup (a power of two)
+  // share their group's block range [g0, g1), and chunk u of the group takes
+  // every p.group-th block of it from g0 + u, so that blocks whose keys are
+  // all padded (a padded tail) spread evenly over the chunks that merge
+  // together.  May be empty if the range has fewer than p.group blocks.
+  const int u = it.chunk & (p.group - 1), lgg = 31 - __builtin_clz((unsigned)p.group);
+  const int g0 = fdiv((it.chunk - u) * p.nb, p.div_chunks);
+  const int g1 = fdiv((it.chunk - u + p.group) * p.nb, p.div_chunks);
+  const int first = g0 + u;
+  const int nblk = middle ? 2 + nw + p.r : std::max(0, (g1 - first + p.group - 1) >> lgg);
   w.n_steps = nblk * w.steps_per_block;
   w.first_blk = middle ? 0 : first;
   int blk;
@@ -202,7 +211,7 @@ __host__ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &i
     if (lane == 1) blk = p.nb - 1;
     else if (lane >= 2 && lane < 2 + nw) blk = (nw == 3) ? (i - 1) + ((lane - 2) - (i - 1) % 3 + 3) % 3 : w0 + (lane - 2);
   } else {
-    blk = first + std::max(std::min(lane, nblk - 1), 0);
+    blk = first + (std::max(std::min(lane, nblk - 1), 0) << lgg);
   }
   w.blk = blk;
   return w;

@@ -51,10 +51,12 @@ def test_multi_gpu_request_is_refused():
 
 def _executed_by_rows(w, mask, plan, chunks):
     """The executed share restated row by row from the pattern itself: a
-    middle row lists block 0 first, a global row's key chunk c covers blocks
-    [c nb / chunks, (c + 1) nb / chunks) and lists its first block first; a
-    list with a key of mask 1 drops its fully padded blocks except the first.
-    (For these workloads each 64-row tile of a query block has the same list.)"""
+    middle row lists block 0 first; a global row's key chunks come in groups
+    of four, group g covering blocks [4g nb / chunks, (4g + 4) nb / chunks),
+    and chunk u of a group lists every fourth block of that range from its
+    u-th; a list with a key of mask 1 drops its fully padded blocks except
+    the first.  (For these workloads each 64-row tile of a query block has
+    the same list.)"""
     nb, blk = w.nb, w.block
     blocks = mask.reshape(w.B, nb, blk)
     padded = (blocks == 0).all(axis=2)
@@ -72,8 +74,10 @@ def _executed_by_rows(w, mask, plan, chunks):
             M = oracle.block_mask(nb, plan[h])
             for i in range(nb):
                 if i in (0, nb - 1):
-                    for c in range(chunks):
-                        add(b, list(range(c * nb // chunks, (c + 1) * nb // chunks)))
+                    for g in range(chunks // 4):
+                        lo, hi = 4 * g * nb // chunks, (4 * g + 4) * nb // chunks
+                        for u in range(4):
+                            add(b, list(range(lo + u, hi, 4)))
                 else:
                     keys = [int(x) for x in np.nonzero(M[i])[0]]
                     add(b, [0] + [x for x in keys if x != 0])
