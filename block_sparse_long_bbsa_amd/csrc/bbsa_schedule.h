@@ -173,11 +173,11 @@ struct KeyWalk {
 // random blocks in, clamped to [0, nb) so that a bad plan never reads outside
 // the sequence.  A middle row lists the two global blocks, its window without
 // them, then its random blocks; a full-row chunk lists every p.group-th block
-// of its group's range (below).  A
-// three-block window is listed by block index mod 3: the four consecutive
-// query blocks of a workgroup have overlapping windows, and this order puts
-// a block they share at the same list position, so their wavefronts fetch
-// it at the same step and the later fetches find it in the caches.
+// of its group's range (below).  A three-block window is listed by block
+// index mod 3: the four consecutive query blocks of a workgroup have
+// overlapping windows, and this order puts a block they share at the same
+// list position, so their wavefronts fetch it at the same step and the later
+// fetches find it in the caches.
 __host__ __device__ inline KeyWalk make_walk_base(const Params &p, const Item &it, int lane, int &rnd,
                                                   int &rslot) {
   KeyWalk w;
