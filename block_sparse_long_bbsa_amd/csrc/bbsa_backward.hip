@@ -789,10 +789,20 @@ __global__ __launch_bounds__(64) void bbsa_bwd_dkdv(BwdParams p) {
     int n = n_fixed;
     const int32_t *plan_h = p.rand_attn + (int64_t)hh * (p.nb - 2) * p.r;
     const int n_entries = (p.nb - 2) * p.r;
+    // The plan is read kScan passes of 64 entries at a time: the loads of
+    // a batch are issued together, then its passes run one after another.
+    constexpr int kScan = 4;
+    int pv[kScan];
     for (int e0 = 0;; e0 += 64) {
+      const int pass = (e0 >> 6) & (kScan - 1);
+      if (pass == 0) {
+#pragma unroll
+        for (int u = 0; u < kScan; ++u) pv[u] = plan_h[min(e0 + 64 * u + lane, n_entries - 1)];
+      }
+      const int pe = pass == 0 ? pv[0] : pass == 1 ? pv[1] : pass == 2 ? pv[2] : pv[3];
       if (e0 < n_entries) {
         const int e = e0 + lane;
-        const bool hit = e < n_entries && min(max(plan_h[min(e, n_entries - 1)], 0), p.nb - 1) == j;
+        const bool hit = e < n_entries && min(max(pe, 0), p.nb - 1) == j;
         unsigned long long bits = __builtin_amdgcn_ballot_w64(hit);
         while (bits) {
           const int l = __builtin_ctzll(bits);
