@@ -98,3 +98,46 @@ def test_executed_pair_fraction(wid, chunks):
         assert got == 1.0     # no padding: nothing is left out
     else:
         assert 0.6 < got < 0.9
+
+
+class _FakeCuda:
+    @staticmethod
+    def synchronize():
+        pass
+
+
+class _FakeTorch:
+    cuda = _FakeCuda()
+
+
+class _FakeRun:
+    torch = _FakeTorch()
+
+    def step(self, i):
+        pass
+
+
+def test_clock_reading_parses_amd_smi(monkeypatch):
+    # The mean of the gfx_* clocks of the one GPU listed; other clock domains
+    # are ignored.
+    out = ('{"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": {"value": 2000, "unit": "MHz"}}, '
+           '"gfx_1": {"clk": {"value": 2100, "unit": "MHz"}}, "mem_0": {"clk": {"value": 1300, "unit": "MHz"}}}}]}')
+    monkeypatch.setattr(bench.subprocess, "run",
+                        lambda *a, **k: bench.subprocess.CompletedProcess(a, 0, stdout=out, stderr=""))
+    res = bench.Runner.clock_under_load(_FakeRun(), 0.2)
+    assert res is not None and res["mhz"] == 2050.0 and res["readings"] >= 1
+
+
+@pytest.mark.parametrize("stdout", ["", "not json", '{"gpu_data": []}',
+                                    '{"gpu_data": [{"clock": {}}, {"clock": {}}]}'])
+def test_clock_reading_is_none_when_unavailable(monkeypatch, stdout):
+    monkeypatch.setattr(bench.subprocess, "run",
+                        lambda *a, **k: bench.subprocess.CompletedProcess(a, 0, stdout=stdout, stderr=""))
+    assert bench.Runner.clock_under_load(_FakeRun(), 0.1) is None
+
+
+def test_clock_reading_without_the_tool(monkeypatch):
+    def missing(*a, **k):
+        raise FileNotFoundError("amd-smi")
+    monkeypatch.setattr(bench.subprocess, "run", missing)
+    assert bench.Runner.clock_under_load(_FakeRun(), 0.1) is None
